@@ -1,0 +1,57 @@
+"""The oracle's pins must catch plausible mistakes (no GPU).
+
+Each case below plants one mistake in a COPY of the oracle's C source, builds it
+into a temporary library and runs the pin suite against it; the suite must fail.
+Nothing here touches the HIP library.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "hc_oracle.c")
+
+MUTANTS = {
+    "rms over d instead of hc*d": ("sumsq / (double)D", "sumsq / (double)d"),
+    "projection not scaled by r": ("(float)(dot * r)", "(float)(dot)"),
+    "norm_eps replaced": ("+ norm_eps);", "+ 1e-6);"),
+    "flatten order channel-major": ("row[c] = load_elem(x, dtype, t * D + c);",
+                                    "row[c] = load_elem(x, dtype, t * D + (c % hc) * d + c / hc);"),
+    "pre without eps": ("+ hc_base[j]) + eps);", "+ hc_base[j]));"),
+    "post without factor 2": ("(float)(2.0 * sigmoid(", "(float)(1.0 * sigmoid("),
+    "pre uses comb scale": ("sigmoid(s0 * m[j]", "sigmoid(s2 * m[j]"),
+    "comb logits transposed": ("int i = 2 * hc + j * hc + k;", "int i = 2 * hc + k * hc + j;"),
+    "softmax without max shift": ("exp(C[j * hc + k] - mx)", "exp(C[j * hc + k])"),
+    "no eps after softmax": ("C[j * hc + k] / s + eps;", "C[j * hc + k] / s;"),
+    "one round too few": ("for (int it = 1; it < sinkhorn_iters; ++it)",
+                          "for (int it = 2; it < sinkhorn_iters; ++it)"),
+    "column step before row step": (
+        "        normalise_rows(C, hc, eps);\n            normalise_cols(C, hc, eps);",
+        "        normalise_cols(C, hc, eps);\n            normalise_rows(C, hc, eps);"),
+    "row normalisation without eps": ("C[j * hc + k] /= (s + eps);", "C[j * hc + k] /= s;"),
+    "collapse uses wrong stream": ("load_elem(x, dtype, (t * hc + j) * d + e)",
+                                   "load_elem(x, dtype, (t * hc + (hc - 1 - j)) * d + e)"),
+    "post sums over comb's second index": ("(double)comb[(t * hc + j) * hc + k]",
+                                           "(double)comb[(t * hc + k) * hc + j]"),
+    "post drops f": ("(double)post[t * hc + k] * load_elem(f, dtype, t * d + e)", "0.0"),
+    "bf16 truncation instead of rounding": ("nearbyint(ldexp(m, 8))", "floor(ldexp(m, 8))"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTANTS[name]
+    text = open(SRC).read()
+    assert text.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    src = tmp_path / "mutant.c"
+    src.write_text(text.replace(old, new, 1))
+    lib = oracle.build(src=str(src), out=str(tmp_path / "libmutant.so"), werror=False)
+    env = dict(os.environ, HC_ORACLE_LIB=lib)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, f"pins did not catch mutant '{name}':\n{r.stdout[-2000:]}"
