@@ -1,0 +1,172 @@
+"""Benchmark of the hyper-connection residual mix on one MI355X.
+
+One step = the hyper-connection work of one DeepSeek-V4.1 block at prefill size
+(B=1, T=4096, 4 streams of d=5120, bf16 streams, fp32 mix parameters), with random
+bf16 stand-ins for the attention and FFN outputs:
+  1. hc_fused_step  attention boundary: coefficients from x, collapse with pi
+  2. hc_fused_step  FFN boundary: x1 = expand(attention output), coefficients from
+                    x1, collapse with attention's pre
+  3. hc_post        x2 = expand(FFN output)
+Inputs are resident in HBM before timing; three independent input sets are cycled
+so that no step re-reads the previous step's data from the 256 MB last-level cache.
+
+Prints one JSON line (see the keys below). --gpus N > 1 is refused: this build runs
+on one GPU.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens/s and achieved HBM TB/s (% of peak), fused HC mix, d=5120, 4 streams"
+PEAK_HBM_GBS = 8000.0
+
+
+def algorithmic_bytes(n: int, d: int, es: int = 2):
+    """Bytes each entry point must move (read + write), counted once each.
+    Coefficients are fp32: pre/post 16 B, comb 64 B per token; hc_fn 24*4d*4 B plus
+    base (96 B) and scale (12 B) once per call."""
+    w = 24 * 4 * d * 4 + 96 + 12
+    k1 = n * (4 * d * es + 16 + d * es + 96) + w                 # x, pi -> y, pre/post/comb
+    k2 = n * (4 * d * es + d * es + 96 + 4 * d * es + d * es + 96) + w   # + f, post/comb/pi -> x1, y
+    k3 = n * (d * es + 4 * d * es + 80 + 4 * d * es)             # f, x1, post/comb -> x2
+    return dict(attn_fused=k1, ffn_fused=k2, ffn_post=k3, block=k1 + k2 + k3)
+
+
+def cpu_baseline(inp):
+    import torch
+
+    import oracle
+
+    x, attn, ffn, fa, ff = inp["x"], inp["attn"], inp["ffn"], inp["f_attn"], inp["f_ffn"]
+    pi, _, _ = oracle.hc_split_sinkhorn(*inp["prev"])
+    cpu = lambda t: t.cpu() if isinstance(t, torch.Tensor) else tuple(u.cpu() for u in t)
+    x, fa, ff, pi, attn, ffn = cpu(x), cpu(fa), cpu(ff), cpu(pi), cpu(attn), cpu(ffn)
+    t0 = time.perf_counter()
+    oracle.block(x, pi, attn, ffn, fa, ff)
+    dt = time.perf_counter() - t0
+    return dict(value=x.shape[0] / dt, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"the full block on one input set ({x.shape[0]} tokens, d={x.shape[-1]}), "
+                       f"single-threaded C oracle, fp64, {dt:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sets", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the per-token work shards across GPUs without communication)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import hc_inputs
+    import hyper_connection_residual_mixes_amd as hc
+
+    dev = torch.device("cuda:0")
+    w = hc_inputs.PREFILL
+    n, d = w.n, w.d
+    print(f"bench: preparing {args.sets} input sets of {w.name}", file=sys.stderr, flush=True)
+    sets = []
+    for s in range(args.sets):
+        inp = hc_inputs.prefill(seed=s, device=dev)
+        pi, _, _ = hc.hc_split_sinkhorn(*inp["prev"])
+        out = dict(yA=torch.empty(n, d, dtype=w.dtype, device=dev),
+                   yF=torch.empty(n, d, dtype=w.dtype, device=dev),
+                   x1=torch.empty(n, 4, d, dtype=w.dtype, device=dev),
+                   x2=torch.empty(n, 4, d, dtype=w.dtype, device=dev),
+                   cA=tuple(torch.empty(sh, device=dev) for sh in ((n, 4), (n, 4), (n, 4, 4))),
+                   cF=tuple(torch.empty(sh, device=dev) for sh in ((n, 4), (n, 4), (n, 4, 4))))
+        sets.append((inp, pi, out))
+        if s == 0:
+            first = inp
+    ws = torch.empty(hc.workspace_size(n, 4, d), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        inp, pi, o = sets[i % len(sets)]
+        if ev is not None:
+            ev[0].record(stream)
+        a = hc.hc_fused_step(inp["x"], *inp["attn"], pre_mix=pi, y=o["yA"], out=o["cA"], workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+        f = hc.hc_fused_step(inp["x"], *inp["ffn"], pre_mix=a["pre"], f_prev=inp["f_attn"],
+                             post_prev=a["post"], comb_prev=a["comb"], streams_out=o["x1"],
+                             y=o["yF"], out=o["cF"], workspace=ws)
+        if ev is not None:
+            ev[2].record(stream)
+        hc.hc_post(inp["f_ffn"], f["streams"], f["post"], f["comb"], out=o["x2"])
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # whole-step timing: K steps bracketed by device synchronisation
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # per-entry-point durations with HIP events on the launch stream (separate pass)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    per = {k: 1e-3 * sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
+           for j, k in enumerate(("attn_fused", "ffn_fused", "ffn_post"))}
+
+    ab = algorithmic_bytes(n, d)
+    ms = 1e3 * wall / args.steps
+    tok_s = n * args.steps / wall
+    eff_gbs = ab["block"] / (wall / args.steps) / 1e9
+    dom = "ffn_fused"
+    ach = ab[dom] / per[dom] / 1e9
+    # plain copy ceiling on the same device (1 GiB read + 1 GiB write)
+    src = torch.empty(1 << 29, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() * 2 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+
+    result = {
+        "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": "prefill block, B=1 T=4096, 4 streams x d=5120, bf16 streams, "
+                               "attention + FFN boundaries", "batch": 1, "seq_len": 4096,
+                   "d": d, "hc": 4, "stream_dtype": "bf16", "input_sets": args.sets},
+        "hbm_effective_gb_s": eff_gbs, "hbm_effective_pct_of_peak": 100 * eff_gbs / PEAK_HBM_GBS,
+        "copy_ceiling_gb_s": copy_gbs,
+        "entry_point_us": {k: v * 1e6 for k, v in per.items()},
+        "algorithmic_bytes": ab,
+        "roofline": {"kernel": "hc_fused_step (FFN boundary: expand + coefficients + collapse)",
+                     "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": ach / PEAK_HBM_GBS, "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle on one input set", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(first)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,240 @@
+"""Python binding of libhc.so, the gfx950 hyper-connection residual mix.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C ABI
+declared in ``include/hc.h``. PyTorch provides device memory (output and workspace
+tensors) and the current HIP stream. There is no fallback: if the library is not
+built, every call raises.
+
+The functions carry the names of the C entry points. Shapes follow the pages'
+``Block`` methods: streams [..., 4, d], sublayer input/output [..., d], mixes
+[..., 24], pre/post [..., 4], comb [..., 4, 4].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhc.so")
+
+HC_F32, HC_BF16 = 0, 1
+HC_MULT, SINKHORN_ITERS, HC_EPS, NORM_EPS = 4, 20, 1e-6, 1e-20
+MIX = (2 + HC_MULT) * HC_MULT
+
+_lib = None
+
+
+class HCError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn}: {text} (status {status})")
+        self.status = status
+
+
+def lib():
+    """The loaded libhc.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                           "(run __graft_entry__.build() or hyper_connection_residual_mixes_amd/build.py)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    L.hc_abi_version.restype = I
+    L.hc_status_string.argtypes = [I]
+    L.hc_status_string.restype = ctypes.c_char_p
+    L.hc_workspace_size.argtypes = [I64, I, I64]
+    L.hc_workspace_size.restype = SZ
+    L.hc_mixes.argtypes = [P, I, I64, I, I64, P, F, P, P, SZ, P]
+    L.hc_split_sinkhorn.argtypes = [P, P, P, I64, I, I, F, P, P, P, P]
+    L.hc_pre.argtypes = [P, I, P, I64, I, I64, P, P]
+    L.hc_post.argtypes = [P, P, I, P, P, I64, I, I64, P, P]
+    L.hc_fused_step.argtypes = [P, P, P, P, P, P, P, P, I64, I, I64, I, F, I, F,
+                                P, P, P, P, P, P, P, SZ, P]
+    for name in ("hc_mixes", "hc_split_sinkhorn", "hc_pre", "hc_post", "hc_fused_step"):
+        getattr(L, name).restype = I
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().hc_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise HCError(fn, status, status_string(status))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return HC_BF16
+    if t.dtype == torch.float32:
+        return HC_F32
+    raise TypeError(f"stream dtype must be bfloat16 or float32, got {t.dtype}")
+
+
+def _dev(t: torch.Tensor, what: str, dtype=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{what} must be a CUDA (HIP) tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{what} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t
+
+
+def _streams_shape(x: torch.Tensor):
+    if x.dim() < 2:
+        raise ValueError("streams must have shape [..., hc, d]")
+    *lead, hc, d = x.shape
+    n = 1
+    for s in lead:
+        n *= s
+    return lead, n, hc, d
+
+
+def workspace_size(n: int, hc: int, d: int) -> int:
+    return int(lib().hc_workspace_size(n, hc, d))
+
+
+def _workspace(n, hc, d, device, workspace):
+    need = workspace_size(n, hc, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def hc_mixes(x, hc_fn, norm_eps=NORM_EPS, out=None, workspace=None):
+    """x [..., hc, d] -> mixes [..., 24] fp32 (projection scaled by the RMS statistic)."""
+    _dev(x, "x")
+    _dev(hc_fn, "hc_fn", torch.float32)
+    lead, n, hc, d = _streams_shape(x)
+    if out is None:
+        out = torch.empty(*lead, (2 + hc) * hc, dtype=torch.float32, device=x.device)
+    _dev(out, "mixes", torch.float32)
+    ws, ws_bytes = _workspace(n, hc, d, x.device, workspace)
+    _check("hc_mixes", lib().hc_mixes(_ptr(x), _dtype_code(x), n, hc, d, _ptr(hc_fn), float(norm_eps),
+                                      _ptr(out), _ptr(ws), ws_bytes, _stream(x.device)))
+    return out
+
+
+def hc_split_sinkhorn(mixes, hc_scale, hc_base, hc_mult=HC_MULT, sinkhorn_iters=SINKHORN_ITERS,
+                      eps=HC_EPS, out=None):
+    """mixes [..., 24] -> (pre [..., 4], post [..., 4], comb [..., 4, 4]), fp32."""
+    _dev(mixes, "mixes", torch.float32)
+    _dev(hc_scale, "hc_scale", torch.float32)
+    _dev(hc_base, "hc_base", torch.float32)
+    *lead, m = mixes.shape
+    n = 1
+    for s in lead:
+        n *= s
+    if out is None:
+        out = (torch.empty(*lead, hc_mult, dtype=torch.float32, device=mixes.device),
+               torch.empty(*lead, hc_mult, dtype=torch.float32, device=mixes.device),
+               torch.empty(*lead, hc_mult, hc_mult, dtype=torch.float32, device=mixes.device))
+    pre, post, comb = (_dev(t, nm, torch.float32) for t, nm in zip(out, ("pre", "post", "comb")))
+    if m != (2 + hc_mult) * hc_mult:
+        raise ValueError(f"mixes last dim must be {(2 + hc_mult) * hc_mult}, got {m}")
+    _check("hc_split_sinkhorn", lib().hc_split_sinkhorn(
+        _ptr(mixes), _ptr(hc_scale), _ptr(hc_base), n, hc_mult, int(sinkhorn_iters), float(eps),
+        _ptr(pre), _ptr(post), _ptr(comb), _stream(mixes.device)))
+    return pre, post, comb
+
+
+def hc_pre(x, pre_mix, out=None):
+    """Collapse: x [..., hc, d], pre_mix [..., hc] -> y [..., d] in x's dtype."""
+    _dev(x, "x")
+    _dev(pre_mix, "pre_mix", torch.float32)
+    lead, n, hc, d = _streams_shape(x)
+    if out is None:
+        out = torch.empty(*lead, d, dtype=x.dtype, device=x.device)
+    _dev(out, "y", x.dtype)
+    _check("hc_pre", lib().hc_pre(_ptr(x), _dtype_code(x), _ptr(pre_mix), n, hc, d, _ptr(out),
+                                  _stream(x.device)))
+    return out
+
+
+def hc_post(f, residual, post, comb, out=None):
+    """Expand and combine: new stream k = post[k] f + sum_j comb[j][k] residual[j]."""
+    _dev(f, "f")
+    _dev(residual, "residual", f.dtype)
+    _dev(post, "post", torch.float32)
+    _dev(comb, "comb", torch.float32)
+    lead, n, hc, d = _streams_shape(residual)
+    if out is None:
+        out = torch.empty_like(residual)
+    _dev(out, "out", f.dtype)
+    _check("hc_post", lib().hc_post(_ptr(f), _ptr(residual), _dtype_code(f), _ptr(post), _ptr(comb), n,
+                                    hc, d, _ptr(out), _stream(f.device)))
+    return out
+
+
+def hc_fused_step(residual, hc_fn, hc_scale, hc_base, pre_mix=None, f_prev=None, post_prev=None,
+                  comb_prev=None, sinkhorn_iters=SINKHORN_ITERS, eps=HC_EPS, norm_eps=NORM_EPS,
+                  streams_out=None, y=None, out=None, want_mixes=False, want_y=True, workspace=None):
+    """One sublayer boundary: optional expand of the previous sublayer's output, then
+    this sublayer's coefficients and the collapse with ``pre_mix``.
+
+    Returns dict(streams, y, pre, post, comb, mixes) (streams is ``residual`` when
+    ``f_prev`` is None; y / mixes are None when not requested)."""
+    _dev(residual, "residual")
+    lead, n, hc, d = _streams_shape(residual)
+    dev = residual.device
+    expand = f_prev is not None
+    if expand:
+        _dev(f_prev, "f_prev", residual.dtype)
+        _dev(post_prev, "post_prev", torch.float32)
+        _dev(comb_prev, "comb_prev", torch.float32)
+        if streams_out is None:
+            streams_out = torch.empty_like(residual)
+        _dev(streams_out, "streams_out", residual.dtype)
+    if want_y:
+        _dev(pre_mix, "pre_mix", torch.float32)
+        if y is None:
+            y = torch.empty(*lead, d, dtype=residual.dtype, device=dev)
+        _dev(y, "y", residual.dtype)
+    else:
+        y = None
+    if out is None:
+        out = (torch.empty(*lead, hc, dtype=torch.float32, device=dev),
+               torch.empty(*lead, hc, dtype=torch.float32, device=dev),
+               torch.empty(*lead, hc, hc, dtype=torch.float32, device=dev))
+    pre, post, comb = out
+    mixes = torch.empty(*lead, (2 + hc) * hc, dtype=torch.float32, device=dev) if want_mixes else None
+    ws, ws_bytes = _workspace(n, hc, d, dev, workspace)
+    _check("hc_fused_step", lib().hc_fused_step(
+        _ptr(residual), _ptr(f_prev), _ptr(post_prev) if expand else None,
+        _ptr(comb_prev) if expand else None, _ptr(pre_mix) if want_y else None,
+        _ptr(_dev(hc_fn, "hc_fn", torch.float32)), _ptr(_dev(hc_scale, "hc_scale", torch.float32)),
+        _ptr(_dev(hc_base, "hc_base", torch.float32)), n, hc, d, _dtype_code(residual),
+        float(norm_eps), int(sinkhorn_iters), float(eps), _ptr(streams_out) if expand else None,
+        _ptr(y), _ptr(pre), _ptr(post), _ptr(comb), _ptr(mixes), _ptr(ws), ws_bytes, _stream(dev)))
+    return dict(streams=streams_out if expand else residual, y=y, pre=pre, post=post, comb=comb,
+                mixes=mixes)
+
+
+def block(x, pre_mix, attn, ffn, f_attn, f_ffn, sinkhorn_iters=SINKHORN_ITERS, eps=HC_EPS,
+          norm_eps=NORM_EPS, x1_out=None, x2_out=None, workspace=None):
+    """The hyper-connection part of one block (attention then FFN boundary) with the
+    sublayer bodies replaced by the given outputs, as three launches-worth of work:
+    fused(attention: coefficients + collapse), fused(expand attention output +
+    FFN coefficients + collapse with attention's pre), expand(FFN output)."""
+    a = hc_fused_step(x, *attn, pre_mix=pre_mix, sinkhorn_iters=sinkhorn_iters, eps=eps,
+                      norm_eps=norm_eps, workspace=workspace)
+    f = hc_fused_step(x, *ffn, pre_mix=a["pre"], f_prev=f_attn, post_prev=a["post"],
+                      comb_prev=a["comb"], sinkhorn_iters=sinkhorn_iters, eps=eps, norm_eps=norm_eps,
+                      streams_out=x1_out, workspace=workspace)
+    x2 = hc_post(f_ffn, f["streams"], f["post"], f["comb"], out=x2_out)
+    return dict(yA=a["y"], preA=a["pre"], postA=a["post"], combA=a["comb"], x1=f["streams"],
+                yF=f["y"], preF=f["pre"], postF=f["post"], combF=f["comb"], x2=x2)

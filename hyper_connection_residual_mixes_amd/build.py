@@ -1,0 +1,39 @@
+"""Compile the HIP library libhc.so for gfx950, in-tree (next to this file)."""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB_PATH = os.path.join(PKG, "libhc.so")
+SOURCES = [os.path.join(CSRC, "hc_kernels.hip"), os.path.join(CSRC, "hc_abi.cpp")]
+
+# Packed-FP32 VALU forms are switched off for all device code.
+HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def build(out: str = LIB_PATH, extra_flags=(), sources=None) -> str:
+    """Always recompiles. Returns the path of the built shared library."""
+    cmd = [hipcc(), *HIP_FLAGS, *extra_flags, "-shared",
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           *(sources or SOURCES), "-o", out + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stderr}")
+    os.replace(out + ".tmp", out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build())

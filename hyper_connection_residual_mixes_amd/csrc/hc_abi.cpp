@@ -1,0 +1,239 @@
+// hc_abi.cpp -- the extern "C" entry points of libhc.so (declared in include/hc.h).
+// Every argument is checked here, before any HIP call; then the launchers in
+// hc_kernels.hip enqueue the work on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "hc.h"
+#include "hc_internal.h"
+
+namespace {
+
+constexpr int kHC = 4;
+constexpr int kMix = 24;
+
+struct Span {
+    const void* p;
+    size_t bytes;
+};
+
+bool overlaps(Span a, Span b) {
+    if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+bool identical(Span a, Span b) { return a.p == b.p && a.bytes == b.bytes; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t elem_size(int dtype) { return dtype == HC_BF16 ? 2 : 4; }
+
+// Shape rules shared by the stream entry points. Returns HC_OK or an error.
+int check_shape(int64_t n, int hc, int64_t d, int dtype) {
+    if (n < 0 || d < 1) return HC_ERR_SHAPE;
+    if (dtype != HC_F32 && dtype != HC_BF16) return HC_ERR_UNSUPPORTED;
+    if (hc != kHC || d % 8 != 0) return HC_ERR_UNSUPPORTED;
+    // every byte offset must fit comfortably in 63 bits
+    if (n > 0 && (uint64_t)d > (uint64_t(1) << 40) / (uint64_t)n) return HC_ERR_SHAPE;
+    return HC_OK;
+}
+
+int check_eps(float v) { return (std::isfinite(v) && v >= 0.f) ? HC_OK : HC_ERR_ARG; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? HC_OK : HC_ERR_HIP; }
+
+// No output may overlap an input or another output, except the listed exact aliases.
+int check_aliases(const Span* outs, int n_out, const Span* ins, int n_in, const Span* allowed_pairs,
+                  int n_allowed) {
+    for (int i = 0; i < n_out; ++i) {
+        for (int j = 0; j < n_in; ++j) {
+            if (!overlaps(outs[i], ins[j])) continue;
+            // only an exact in-place alias of a listed (output, input) pair is allowed
+            bool ok = false;
+            for (int k = 0; k + 1 < 2 * n_allowed; k += 2)
+                if (identical(outs[i], ins[j]) && identical(outs[i], allowed_pairs[k]) &&
+                    identical(ins[j], allowed_pairs[k + 1]))
+                    ok = true;
+            if (!ok) return HC_ERR_ALIAS;
+        }
+        for (int j = i + 1; j < n_out; ++j)
+            if (overlaps(outs[i], outs[j])) return HC_ERR_ALIAS;
+    }
+    return HC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hc_abi_version(void) { return HC_ABI_VERSION; }
+
+const char* hc_status_string(int status) {
+    switch (status) {
+        case HC_OK: return "ok";
+        case HC_ERR_NULL: return "a required pointer is NULL";
+        case HC_ERR_SHAPE: return "invalid shape (n < 0, d < 1 or too large)";
+        case HC_ERR_UNSUPPORTED: return "unsupported configuration (hc must be 4, d a multiple of 8, dtype fp32 or bf16)";
+        case HC_ERR_ALIGN: return "misaligned pointer (16 bytes required)";
+        case HC_ERR_ARG: return "invalid argument (sinkhorn_iters < 1, or eps/norm_eps negative or not finite)";
+        case HC_ERR_ALIAS: return "an output overlaps an input or another output";
+        case HC_ERR_WORKSPACE: return "workspace missing or too small";
+        case HC_ERR_HIP: return "the HIP runtime reported an error";
+        default: return "unknown status";
+    }
+}
+
+size_t hc_workspace_size(int64_t n, int hc, int64_t d) {
+    if (n <= 0 || check_shape(n, hc, d, HC_F32) != HC_OK) return 0;
+    return hc::plan_pass(n, d).workspace_bytes;
+}
+
+int hc_split_sinkhorn(const float* mixes, const float* hc_scale, const float* hc_base, int64_t n, int hc,
+                      int sinkhorn_iters, float eps, float* pre, float* post, float* comb, void* stream) {
+    if (n < 0) return HC_ERR_SHAPE;
+    if (hc != kHC) return HC_ERR_UNSUPPORTED;
+    if (sinkhorn_iters < 1 || check_eps(eps) != HC_OK) return HC_ERR_ARG;
+    if (n == 0) return HC_OK;
+    if (!mixes || !hc_scale || !hc_base || !pre || !post || !comb) return HC_ERR_NULL;
+    if (!aligned(mixes, 16) || !aligned(pre, 16) || !aligned(post, 16) || !aligned(comb, 16) ||
+        !aligned(hc_scale, 4) || !aligned(hc_base, 4))
+        return HC_ERR_ALIGN;
+    const size_t un = (size_t)n;
+    const Span outs[] = {{pre, un * 16}, {post, un * 16}, {comb, un * 64}};
+    const Span ins[] = {{mixes, un * kMix * 4}, {hc_scale, 12}, {hc_base, kMix * 4}};
+    if (int rc = check_aliases(outs, 3, ins, 3, nullptr, 0)) return rc;
+    return hip_status(hc::launch_split(mixes, hc_scale, hc_base, n, sinkhorn_iters, eps, pre, post, comb,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int hc_pre(const void* x, int dtype, const float* pre_mix, int64_t n, int hc, int64_t d, void* y,
+           void* stream) {
+    if (int rc = check_shape(n, hc, d, dtype)) return rc;
+    if (n == 0) return HC_OK;
+    if (!x || !pre_mix || !y) return HC_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(pre_mix, 16) || !aligned(y, 16)) return HC_ERR_ALIGN;
+    const size_t es = elem_size(dtype), un = (size_t)n, ud = (size_t)d;
+    const Span outs[] = {{y, un * ud * es}};
+    const Span ins[] = {{x, un * kHC * ud * es}, {pre_mix, un * 16}};
+    if (int rc = check_aliases(outs, 1, ins, 2, nullptr, 0)) return rc;
+    return hip_status(hc::launch_pre(x, dtype == HC_BF16, pre_mix, n, d, y, static_cast<hipStream_t>(stream)));
+}
+
+int hc_post(const void* f, const void* residual, int dtype, const float* post, const float* comb, int64_t n,
+            int hc, int64_t d, void* out, void* stream) {
+    if (int rc = check_shape(n, hc, d, dtype)) return rc;
+    if (n == 0) return HC_OK;
+    if (!f || !residual || !post || !comb || !out) return HC_ERR_NULL;
+    if (!aligned(f, 16) || !aligned(residual, 16) || !aligned(post, 16) || !aligned(comb, 16) ||
+        !aligned(out, 16))
+        return HC_ERR_ALIGN;
+    const size_t es = elem_size(dtype), un = (size_t)n, ud = (size_t)d;
+    const Span res_span{residual, un * kHC * ud * es};
+    const Span outs[] = {{out, un * kHC * ud * es}};
+    const Span ins[] = {{f, un * ud * es}, res_span, {post, un * 16}, {comb, un * 64}};
+    const Span allowed[] = {outs[0], res_span};
+    if (int rc = check_aliases(outs, 1, ins, 4, allowed, 1)) return rc;
+    return hip_status(hc::launch_post(f, residual, dtype == HC_BF16, post, comb, n, d, out,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int hc_mixes(const void* x, int dtype, int64_t n, int hc, int64_t d, const float* hc_fn, float norm_eps,
+             float* mixes, void* workspace, size_t workspace_bytes, void* stream) {
+    if (int rc = check_shape(n, hc, d, dtype)) return rc;
+    if (check_eps(norm_eps) != HC_OK) return HC_ERR_ARG;
+    if (n == 0) return HC_OK;
+    if (!x || !hc_fn || !mixes) return HC_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(hc_fn, 16) || !aligned(mixes, 16)) return HC_ERR_ALIGN;
+    const hc::PassPlan plan = hc::plan_pass(n, d);
+    if (!workspace || workspace_bytes < plan.workspace_bytes) return HC_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return HC_ERR_ALIGN;
+    const size_t es = elem_size(dtype), un = (size_t)n, ud = (size_t)d;
+    const Span outs[] = {{mixes, un * kMix * 4}, {workspace, plan.workspace_bytes}};
+    const Span ins[] = {{x, un * kHC * ud * es}, {hc_fn, (size_t)kMix * kHC * ud * 4}};
+    if (int rc = check_aliases(outs, 2, ins, 2, nullptr, 0)) return rc;
+    hc::PassRequest r{};
+    r.res = x;
+    r.hc_fn = hc_fn;
+    r.mixes = mixes;
+    r.workspace = workspace;
+    r.n = n;
+    r.d = d;
+    r.bf16 = dtype == HC_BF16;
+    r.split = false;
+    r.norm_eps = norm_eps;
+    r.iters = 1;
+    return hip_status(hc::launch_pass_and_finalize(r, static_cast<hipStream_t>(stream)));
+}
+
+int hc_fused_step(const void* residual, const void* f_prev, const float* post_prev, const float* comb_prev,
+                  const float* pre_mix, const float* hc_fn, const float* hc_scale, const float* hc_base,
+                  int64_t n, int hc, int64_t d, int dtype, float norm_eps, int sinkhorn_iters, float eps,
+                  void* streams_out, void* y, float* pre, float* post, float* comb, float* mixes,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+    if (int rc = check_shape(n, hc, d, dtype)) return rc;
+    if (check_eps(norm_eps) != HC_OK || check_eps(eps) != HC_OK || sinkhorn_iters < 1) return HC_ERR_ARG;
+    if (n == 0) return HC_OK;
+    if (!residual || !hc_fn || !hc_scale || !hc_base || !pre || !post || !comb) return HC_ERR_NULL;
+    const bool expand = f_prev != nullptr;
+    if (expand && (!post_prev || !comb_prev || !streams_out)) return HC_ERR_NULL;
+    if (y && !pre_mix) return HC_ERR_NULL;
+    const hc::PassPlan plan = hc::plan_pass(n, d);
+    if (!workspace || workspace_bytes < plan.workspace_bytes) return HC_ERR_WORKSPACE;
+    const void* a16[] = {residual, hc_fn, pre, post, comb, workspace};
+    for (const void* p : a16)
+        if (!aligned(p, 16)) return HC_ERR_ALIGN;
+    const void* o16[] = {f_prev, post_prev, comb_prev, pre_mix, streams_out, y, mixes};
+    for (const void* p : o16)
+        if (p && !aligned(p, 16)) return HC_ERR_ALIGN;
+    if (!aligned(hc_scale, 4) || !aligned(hc_base, 4)) return HC_ERR_ALIGN;
+
+    const size_t es = elem_size(dtype), un = (size_t)n, ud = (size_t)d;
+    const Span res_span{residual, un * kHC * ud * es};
+    const Span so_span{expand ? streams_out : nullptr, un * kHC * ud * es};
+    const Span outs[] = {so_span,
+                         {y, un * ud * es},
+                         {pre, un * 16},
+                         {post, un * 16},
+                         {comb, un * 64},
+                         {mixes, un * kMix * 4},
+                         {workspace, plan.workspace_bytes}};
+    const Span ins[] = {res_span,
+                        {f_prev, un * ud * es},
+                        {expand ? post_prev : nullptr, un * 16},
+                        {expand ? comb_prev : nullptr, un * 64},
+                        {y ? pre_mix : nullptr, un * 16},
+                        {hc_fn, (size_t)kMix * kHC * ud * 4},
+                        {hc_scale, 12},
+                        {hc_base, kMix * 4}};
+    const Span allowed[] = {so_span, res_span};
+    if (int rc = check_aliases(outs, 7, ins, 8, allowed, 1)) return rc;
+
+    hc::PassRequest r{};
+    r.res = residual;
+    r.f_prev = f_prev;
+    r.post_prev = post_prev;
+    r.comb_prev = comb_prev;
+    r.pre_mix = pre_mix;
+    r.hc_fn = hc_fn;
+    r.scale = hc_scale;
+    r.base = hc_base;
+    r.streams_out = expand ? streams_out : nullptr;
+    r.y = y;
+    r.mixes = mixes;
+    r.pre = pre;
+    r.post = post;
+    r.comb = comb;
+    r.workspace = workspace;
+    r.n = n;
+    r.d = d;
+    r.bf16 = dtype == HC_BF16;
+    r.split = true;
+    r.norm_eps = norm_eps;
+    r.iters = sinkhorn_iters;
+    r.eps = eps;
+    return hip_status(hc::launch_pass_and_finalize(r, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

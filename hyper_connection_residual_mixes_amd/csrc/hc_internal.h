@@ -1,0 +1,56 @@
+// hc_internal.h -- launchers behind the C ABI (not part of the public interface).
+// Callers have validated every argument; these functions only enqueue kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hc {
+
+// How one sweep over n tokens x d channels is cut into workgroups: `tiles`
+// tiles of 64 tokens times `nsplit` channel slices of `chunks_per_split`
+// 32-channel steps. Each (slice, token) writes one 32-float partial row.
+struct PassPlan {
+    int64_t tiles;
+    int nchunks;
+    int chunks_per_split;
+    int nsplit;
+    size_t workspace_bytes;
+};
+PassPlan plan_pass(int64_t n, int64_t d);
+
+struct PassRequest {
+    const void* res;         // streams entering the boundary [n][4][d]
+    const void* f_prev;      // previous sublayer output [n][d], or null (no expand)
+    const float* post_prev;  // [n][4]
+    const float* comb_prev;  // [n][4][4]
+    const float* pre_mix;    // [n][4] collapse weights (used when y != null)
+    const float* hc_fn;      // [24][4d]
+    const float* scale;      // [3]
+    const float* base;       // [24]
+    void* streams_out;       // [n][4][d] when f_prev != null
+    void* y;                 // [n][d] or null
+    float* mixes;            // [n][24] or null
+    float* pre;              // [n][4]   (split only)
+    float* post;             // [n][4]   (split only)
+    float* comb;             // [n][4][4] (split only)
+    void* workspace;         // >= plan_pass(n, d).workspace_bytes
+    int64_t n;
+    int64_t d;
+    bool bf16;
+    bool split;              // run split + Sinkhorn after the projection
+    float norm_eps;
+    int iters;
+    float eps;
+};
+
+hipError_t launch_split(const float* mixes, const float* scale, const float* base, int64_t n, int iters,
+                        float eps, float* pre, float* post, float* comb, hipStream_t stream);
+hipError_t launch_pre(const void* x, bool bf16, const float* pre_mix, int64_t n, int64_t d, void* y,
+                      hipStream_t stream);
+hipError_t launch_post(const void* f, const void* res, bool bf16, const float* post, const float* comb,
+                       int64_t n, int64_t d, void* out, hipStream_t stream);
+hipError_t launch_pass_and_finalize(const PassRequest& r, hipStream_t stream);
+
+}  // namespace hc

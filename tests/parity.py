@@ -1,0 +1,51 @@
+"""Comparison rule shared by the GPU parity tests (not a test module).
+
+An element passes when |got - ref| <= tol * max(|ref|, rho), where rho guards values
+that cancel to near zero: the RMS of the reference token's row for streams, the
+collapsed input and the mixes; 1 for the coefficients pre, post and comb, which are
+O(1) by construction (comb entries lie in [0, 1] and its columns sum to one).
+
+Tolerances: 1e-5 for fp32 results computed from exact inputs, 2e-2 for results of
+bf16 stream configurations (the bf16 spacing is 2^-8 relative, so one rounding
+difference is far inside it).
+"""
+import sys
+
+import torch
+
+TOL_F32 = 1e-5
+TOL_BF16 = 2e-2
+
+
+def max_rel_err(got: torch.Tensor, ref: torch.Tensor, rho="row", tokens_dims=1) -> float:
+    g = got.detach().to("cpu", torch.float64)
+    r = ref.detach().to("cpu", torch.float64)
+    assert g.shape == r.shape, (tuple(g.shape), tuple(r.shape))
+    if g.numel() == 0:
+        return 0.0
+    if not torch.isfinite(g).all():
+        return float("inf")
+    lead = 1
+    for s in r.shape[:tokens_dims]:
+        lead *= s
+    g2, r2 = g.reshape(lead, -1), r.reshape(lead, -1)
+    if rho == "row":
+        rho_t = r2.pow(2).mean(1, keepdim=True).sqrt()
+    else:
+        rho_t = torch.full((lead, 1), float(rho), dtype=torch.float64)
+    return ((g2 - r2).abs() / torch.maximum(r2.abs(), rho_t)).max().item()
+
+
+def check(name: str, got, ref, tol: float, rho="row", tokens_dims=1) -> float:
+    err = max_rel_err(got, ref, rho, tokens_dims)
+    print(f"  {name:<28s} max rel err {err:.3e} (tol {tol:g})", flush=True)
+    sys.stdout.flush()
+    assert err <= tol, f"{name}: max relative error {err:.3e} > {tol:g}"
+    return err
+
+
+def rho_for(key: str):
+    k = key.lower()
+    if k.startswith(("pre", "post", "comb")) or k.endswith(("pre", "post", "comb")):
+        return 1.0
+    return "row"

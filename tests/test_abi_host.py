@@ -1,0 +1,161 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point the
+header declares, and rejects bad arguments before any HIP call.
+
+Pointers passed here are fake addresses; every call below must fail validation, so
+none of them reaches a kernel launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import torch
+
+import hyper_connection_residual_mixes_amd as hc
+
+# Fake addresses must never reach a device: these tests run only where no GPU exists.
+pytestmark = pytest.mark.skipif(torch.cuda.is_available(),
+                                reason="host-only validation tests (fake device pointers)")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hc.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, ARG, ALIAS, WS, HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8
+P = ctypes.c_void_p
+A = 0x10000000          # a 16-byte aligned fake address
+B = 0x20000000
+C = 0x30000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[a-z_ ]+[ *]+(hc_[a-z_]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("hc_mixes", "hc_split_sinkhorn", "hc_pre", "hc_post", "hc_fused_step",
+                 "hc_workspace_size", "hc_status_string", "hc_abi_version"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = hc.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings():
+    L = hc.lib()
+    assert L.hc_abi_version() == 1
+    for s in range(-8, 1):
+        assert hc.status_string(s) and hc.status_string(s) != "unknown status"
+    assert hc.status_string(-99) == "unknown status"
+
+
+def test_workspace_size_rule():
+    # 64-token tiles x 32-channel steps; one 128-byte partial row per (slice, token)
+    assert hc.workspace_size(0, 4, 5120) == 0
+    assert hc.workspace_size(16, 3, 5120) == 0
+    assert hc.workspace_size(16, 4, 12) == 0
+    for n, d in ((16, 256), (64, 5120), (4096, 5120), (65536, 5120), (37, 264)):
+        ws = hc.workspace_size(n, 4, d)
+        assert ws > 0 and ws % (128 * n) == 0
+        nsplit = ws // (128 * n)
+        assert 1 <= nsplit <= min(64, -(-d // 32))
+
+
+def _split(mixes=A, scale=B, base=C, n=16, hc_=4, iters=20, eps=1e-6, pre=A + 4096, post=A + 8192,
+           comb=A + 16384):
+    return hc.lib().hc_split_sinkhorn(P(mixes), P(scale), P(base), n, hc_, iters, eps, P(pre), P(post),
+                                      P(comb), None)
+
+
+def test_split_validation():
+    assert _split(n=0) == OK            # no-op touches nothing
+    assert _split(n=-1) == SHAPE
+    assert _split(hc_=3) == UNSUP
+    assert _split(iters=0) == ARG
+    assert _split(eps=-1.0) == ARG
+    assert _split(eps=float("nan")) == ARG
+    assert _split(mixes=None) == NULL
+    assert _split(mixes=A + 4) == ALIGN
+    assert _split(pre=A) == ALIAS        # pre overlaps mixes
+    assert _split(comb=A + 4096) == ALIAS  # comb overlaps pre
+
+
+def _pre(x=A, dtype=1, pm=B, n=16, hc_=4, d=256, y=C):
+    return hc.lib().hc_pre(P(x), dtype, P(pm), n, hc_, d, P(y), None)
+
+
+def test_pre_validation():
+    assert _pre(n=0) == OK
+    assert _pre(d=0) == SHAPE
+    assert _pre(d=260) == UNSUP
+    assert _pre(dtype=2) == UNSUP
+    assert _pre(hc_=2) == UNSUP
+    assert _pre(x=None) == NULL
+    assert _pre(y=C + 2) == ALIGN
+    assert _pre(y=A + 1024) == ALIAS
+
+
+def _post(f=A, res=B, dtype=1, post=C, comb=C + 4096, n=16, d=256, out=0x40000000):
+    return hc.lib().hc_post(P(f), P(res), dtype, P(post), P(comb), n, 4, d, P(out), None)
+
+
+def test_post_validation():
+    assert _post(n=0) == OK
+    assert _post(f=None) == NULL
+    assert _post(comb=C + 8) == ALIGN
+    assert _post(out=B + 16) == ALIAS    # partial overlap with residual
+    assert _post(out=A) == ALIAS         # overlaps f
+
+
+def _mixes(x=A, n=16, d=256, fn=B, norm_eps=1e-20, mixes=C, ws=0x40000000, ws_bytes=1 << 20):
+    return hc.lib().hc_mixes(P(x), 1, n, 4, d, P(fn), norm_eps, P(mixes), P(ws), ws_bytes, None)
+
+
+def test_mixes_validation():
+    assert _mixes(n=0) == OK
+    assert _mixes(norm_eps=-1.0) == ARG
+    assert _mixes(ws=None) == WS
+    assert _mixes(ws_bytes=hc.workspace_size(16, 4, 256) - 1) == WS
+    assert _mixes(ws=0x40000008) == ALIGN
+    assert _mixes(mixes=A + 256) == ALIAS
+    assert _mixes(ws=C) == ALIAS
+
+
+def _fused(res=A, f_prev=None, post_prev=None, comb_prev=None, pre_mix=0x50000000, fn=B, scale=C,
+           base=C + 64, n=16, d=256, dtype=1, iters=20, so=None, y=0x60000000, pre=0x70000000,
+           post=0x70001000, comb=0x70002000, mixes=None, ws=0x40000000, ws_bytes=1 << 20):
+    return hc.lib().hc_fused_step(P(res), P(f_prev), P(post_prev), P(comb_prev), P(pre_mix), P(fn),
+                                  P(scale), P(base), n, 4, d, dtype, 1e-20, iters, 1e-6, P(so), P(y),
+                                  P(pre), P(post), P(comb), P(mixes), P(ws), ws_bytes, None)
+
+
+def test_fused_validation():
+    assert _fused(n=0) == OK
+    assert _fused(iters=0) == ARG
+    assert _fused(pre=None) == NULL
+    assert _fused(f_prev=0x58000000) == NULL                       # expand needs post/comb/out
+    assert _fused(pre_mix=None) == NULL                            # a collapse needs pre_mix
+    assert _fused(ws_bytes=16) == WS
+    assert _fused(scale=C + 2) == ALIGN
+    assert _fused(y=A + 64) == ALIAS                               # y inside residual
+    assert _fused(f_prev=0x58000000, post_prev=0x59000000, comb_prev=0x59001000,
+                  so=A + 16) == ALIAS                              # partial overlap with residual
+    assert _fused(mixes=0x70000080) == ALIAS                       # mixes inside pre
+
+
+@pytest.mark.parametrize("fn", ["hc_pre", "hc_post", "hc_mixes", "hc_fused_step"])
+def test_huge_shapes_rejected(fn):
+    if fn == "hc_pre":
+        assert _pre(n=1 << 40, d=1 << 20) == SHAPE
+    elif fn == "hc_post":
+        assert _post(n=1 << 40, d=1 << 20) == SHAPE
+    elif fn == "hc_mixes":
+        assert _mixes(n=1 << 40, d=1 << 20) == SHAPE
+    else:
+        assert _fused(n=1 << 40, d=1 << 20) == SHAPE

@@ -1,0 +1,206 @@
+"""GPU parity: every C-ABI entry point against the CPU oracle on the same seeded inputs.
+
+Sizes: the tiny fp32 block, ragged sizes that leave partial 64-token tiles and a
+partial 32-channel step, the full decode block (64 x 5120) and the full prefill block
+(4096 x 5120, the benchmark's launch configuration), and the full 1,048,576-row
+Sinkhorn stress set. Tolerances and the comparison rule are in tests/parity.py.
+"""
+import pytest
+import torch
+
+import hc_inputs
+import hyper_connection_residual_mixes_amd as hc
+import oracle
+from parity import TOL_BF16, TOL_F32, check, rho_for
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def to_dev(t):
+    return t.to(DEV) if isinstance(t, torch.Tensor) else tuple(to_dev(u) for u in t)
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+def oracle_pi(inp):
+    """Collapse weights handed over by a previous sublayer: the oracle's split of the
+    previous call's logits (drawn by the input generator)."""
+    pre, _, _ = oracle.hc_split_sinkhorn(*inp["prev"])
+    return pre
+
+
+# -------------------------------------------------------------------- split
+def test_split_stress_full():
+    """All 1,048,576 rows of the Sinkhorn stress workload (5% with a +40 comb logit)."""
+    st = hc_inputs.stress(seed=0)
+    ref = oracle.hc_split_sinkhorn(st["mixes"], st["scale"], st["base"])
+    got = hc.hc_split_sinkhorn(*to_dev((st["mixes"], st["scale"], st["base"])))
+    sync()
+    for name, g, r in zip(("pre", "post", "comb"), got, ref):
+        check(f"stress {name}", g, r, TOL_F32, rho=1.0)
+    col = got[2].double().sum(1).cpu()
+    assert (col - 1).abs().max().item() < 2.5e-6   # the last step normalises columns
+
+
+@pytest.mark.parametrize("n", [1, 255, 257, 1000])
+@pytest.mark.parametrize("iters", [1, 20])
+def test_split_ragged_rows_and_rounds(n, iters):
+    g = hc_inputs.generator(5)
+    m = hc_inputs.normal(g, (n, 24), 2.0)
+    s = torch.rand(3, generator=g) * 1.5 + 0.5
+    b = hc_inputs.normal(g, (24,), 0.1)
+    ref = oracle.hc_split_sinkhorn(m, s, b, sinkhorn_iters=iters)
+    got = hc.hc_split_sinkhorn(*to_dev((m, s, b)), sinkhorn_iters=iters)
+    sync()
+    for name, gg, r in zip(("pre", "post", "comb"), got, ref):
+        check(f"n={n} it={iters} {name}", gg, r, TOL_F32, rho=1.0)
+
+
+# ------------------------------------------------------------- pre / post
+CASES = [(torch.float32, 16, 256), (torch.float32, 37, 264), (torch.bfloat16, 37, 264),
+         (torch.bfloat16, 1, 8), (torch.bfloat16, 64, 5120)]
+
+
+def _streams_case(dtype, n, d, seed=1):
+    g = hc_inputs.generator(seed)
+    x = hc_inputs.streams(g, n, 4, d, dtype, outlier_frac=0.1)
+    f = hc_inputs.sublayer_output(g, n, d, dtype)
+    w = torch.rand(n, 4, generator=g)
+    post = torch.rand(n, 4, generator=g) * 2
+    comb = torch.rand(n, 4, 4, generator=g)
+    return x, f, w, post, comb
+
+
+@pytest.mark.parametrize("dtype,n,d", CASES)
+def test_pre(dtype, n, d):
+    x, _, w, _, _ = _streams_case(dtype, n, d)
+    got = hc.hc_pre(*to_dev((x, w)))
+    sync()
+    assert got.dtype == dtype
+    check(f"pre {dtype} {n}x{d}", got, oracle.hc_pre(x, w),
+          TOL_F32 if dtype == torch.float32 else TOL_BF16)
+
+
+@pytest.mark.parametrize("dtype,n,d", CASES)
+def test_post_and_in_place(dtype, n, d):
+    x, f, _, post, comb = _streams_case(dtype, n, d)
+    ref = oracle.hc_post(f, x, post, comb)
+    tol = TOL_F32 if dtype == torch.float32 else TOL_BF16
+    xd, fd, pd, cd = to_dev((x, f, post, comb))
+    got = hc.hc_post(fd, xd, pd, cd)
+    sync()
+    check(f"post {dtype} {n}x{d}", got, ref, tol)
+    hc.hc_post(fd, xd, pd, cd, out=xd)          # exact in-place
+    sync()
+    assert torch.equal(xd.cpu(), got.cpu())
+
+
+# ------------------------------------------------------------------- mixes
+@pytest.mark.parametrize("dtype,n,d", CASES)
+def test_mixes(dtype, n, d):
+    g = hc_inputs.generator(2)
+    fn, _, _ = hc_inputs.mix_params(g, 4, d, "ones")
+    x = hc_inputs.streams(g, n, 4, d, dtype, outlier_frac=0.1)
+    ref = oracle.hc_mixes(x, fn)
+    xd, fnd = to_dev((x, fn))
+    ws = torch.full((hc.workspace_size(n, 4, d),), 255, dtype=torch.uint8, device=DEV)  # NaN bytes
+    got = hc.hc_mixes(xd, fnd, workspace=ws)
+    sync()
+    check(f"mixes {dtype} {n}x{d}", got, ref, TOL_F32)
+
+
+# ----------------------------------------------------------- fused / block
+def _block_check(inp, tol_streams, tol_coef_k2):
+    x = inp["x"]
+    pi = oracle_pi(inp)
+    ref = oracle.block(x, pi, inp["attn"], inp["ffn"], inp["f_attn"], inp["f_ffn"])
+    got = hc.block(*to_dev((x, pi)), to_dev(inp["attn"]), to_dev(inp["ffn"]),
+                   *to_dev((inp["f_attn"], inp["f_ffn"])))
+    sync()
+    # attention boundary: coefficients from the given streams -> fp32 tolerance
+    for k in ("preA", "postA", "combA"):
+        check(k, got[k], ref[k], TOL_F32, rho=1.0)
+    for k in ("yA", "x1", "yF", "x2"):
+        check(k, got[k], ref[k], tol_streams)
+    # FFN boundary: coefficients from the rounded new streams x1 (see module doc)
+    for k in ("preF", "postF", "combF"):
+        check(k, got[k], ref[k], tol_coef_k2, rho=1.0)
+    return ref
+
+
+def test_block_tiny_fp32():
+    """fp32 streams: every output of the block within 1e-5."""
+    _block_check(hc_inputs.tiny(seed=0), TOL_F32, TOL_F32)
+
+
+@pytest.mark.parametrize("which", ["decode", "prefill"])
+def test_block_bf16_full(which):
+    """The full decode (64 tokens) and prefill (4096 tokens, 1% x50 outliers) blocks.
+    bf16 results within 2e-2. The FFN coefficients are computed from the bf16-rounded
+    streams x1; a value the two sides round to neighbouring bf16 numbers shifts the
+    mixes by ~3e-5, so they are held to the bf16 tolerance here and to 1e-5 in
+    test_fused_coefficients_exact_inputs, where both sides get the same streams."""
+    inp = hc_inputs.decode(seed=0) if which == "decode" else hc_inputs.prefill(seed=0)
+    ref = _block_check(inp, TOL_BF16, TOL_BF16)
+    assert ref["x2"].dtype == torch.bfloat16
+
+
+@pytest.mark.parametrize("which", ["tiny", "decode", "prefill"])
+def test_fused_coefficients_exact_inputs(which):
+    """hc_fused_step without the expand step, on streams both sides receive exactly
+    (the oracle's own x1 of the block): pre/post/comb and mixes within 1e-5."""
+    inp = {"tiny": hc_inputs.tiny, "decode": hc_inputs.decode, "prefill": hc_inputs.prefill}[which](seed=0)
+    pi = oracle_pi(inp)
+    x1 = oracle.hc_post(inp["f_attn"], inp["x"],
+                        *oracle.hc_split_sinkhorn(oracle.hc_mixes(inp["x"], inp["attn"][0]),
+                                                  inp["attn"][1], inp["attn"][2])[1:])
+    ref = oracle.fused_step(x1, *inp["ffn"], pre_mix=pi)
+    got = hc.hc_fused_step(*to_dev((x1,)), *to_dev(inp["ffn"]), pre_mix=to_dev(pi), want_mixes=True)
+    sync()
+    for k in ("mixes", "pre", "post", "comb"):
+        check(f"{which} {k}", got[k], ref[k], TOL_F32, rho=rho_for(k))
+    check(f"{which} y", got["y"], ref["y"], TOL_F32 if x1.dtype == torch.float32 else TOL_BF16)
+
+
+@pytest.mark.parametrize("dtype,n,d", [(torch.float32, 37, 264), (torch.bfloat16, 37, 264),
+                                       (torch.bfloat16, 1, 8), (torch.bfloat16, 130, 5120)])
+def test_fused_expand_ragged_and_in_place(dtype, n, d):
+    """Fused step with the expand step, at ragged sizes, out of place and in place."""
+    g = hc_inputs.generator(11)
+    fn, s, b = hc_inputs.mix_params(g, 4, d, "uniform")
+    x, f, w, post, comb = _streams_case(dtype, n, d, seed=12)
+    ref = oracle.fused_step(x, fn, s, b, pre_mix=w, f_prev=f, post_prev=post, comb_prev=comb)
+    tol_s = TOL_F32 if dtype == torch.float32 else TOL_BF16
+    args = to_dev((x, fn, s, b))
+    kw = dict(pre_mix=to_dev(w), f_prev=to_dev(f), post_prev=to_dev(post), comb_prev=to_dev(comb),
+              want_mixes=True)
+    got = hc.hc_fused_step(*args, **kw)
+    sync()
+    check("streams", got["streams"], ref["streams"], tol_s)
+    check("y", got["y"], ref["y"], tol_s)
+    for k in ("mixes", "pre", "post", "comb"):
+        check(k, got[k], ref[k], tol_s, rho=rho_for(k))
+    xd = args[0]
+    got2 = hc.hc_fused_step(*args, **kw, streams_out=xd)   # exact in-place
+    sync()
+    assert torch.equal(xd.cpu(), got["streams"].cpu())
+    for k in ("y", "mixes", "pre", "post", "comb"):
+        assert torch.equal(got2[k].cpu(), got[k].cpu()), k
+
+
+def test_fused_deterministic_and_zero_tokens():
+    """Two runs of the prefill attention boundary are bit-identical; n = 0 is a no-op."""
+    inp = hc_inputs.prefill(seed=1)
+    pi = to_dev(oracle_pi(inp))
+    xd = to_dev(inp["x"])
+    a = hc.hc_fused_step(xd, *to_dev(inp["attn"]), pre_mix=pi, want_mixes=True)
+    b = hc.hc_fused_step(xd, *to_dev(inp["attn"]), pre_mix=pi, want_mixes=True)
+    sync()
+    for k in ("y", "mixes", "pre", "post", "comb"):
+        assert torch.equal(a[k], b[k]), k
+    e = hc.hc_fused_step(xd[:0], *to_dev(inp["attn"]), pre_mix=pi[:0])
+    sync()
+    assert e["pre"].numel() == 0
