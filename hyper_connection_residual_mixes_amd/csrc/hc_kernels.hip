@@ -15,7 +15,7 @@
 //                       optional expand (previous sublayer's post/comb), optional
 //                       collapse, and the partial 24-wide projection + sum of
 //                       squares of the (rounded) streams, written to a workspace.
-//   finalize_kernel     one lane per token: reduce the slice partials in a fixed
+//   finalize_kernel     16 lanes per token: reduce the slice partials in a fixed
 //                       order, scale by the RMS statistic, and (optionally) split.
 //
 // All arithmetic is fp32. bf16 values are rounded to nearest-even
@@ -36,8 +36,15 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 constexpr int kHC = 4;          // streams
 constexpr int kMix = 24;        // (2 + hc) * hc mix numbers
 constexpr int kPart = 32;       // floats per (split, token) partial row: 24 dots, sumsq, pad
-constexpr int kWaves = 4;       // waves per pass workgroup
-constexpr int kTokWave = 16;    // tokens per wave (one MFMA row tile)
+#ifndef HC_TILES
+#define HC_TILES 1
+#endif
+#ifndef HC_TARGET_GROUPS
+#define HC_TARGET_GROUPS 512
+#endif
+constexpr int kWaves = 4;           // waves per pass workgroup
+constexpr int kTiles = HC_TILES;    // 16-token MFMA row tiles per wave
+constexpr int kTokWave = 16 * kTiles;
 constexpr int kTokWG = kWaves * kTokWave;
 constexpr int kChunk = 32;      // channels per sweep step (4 lane groups x 8)
 
@@ -48,6 +55,33 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// ------------------------------------------------------------- buffer access
+// Raw buffer loads/stores (MUBUF): a wave-uniform 128-bit resource (base, byte
+// range) plus a per-lane 32-bit offset and a uniform scalar offset. A lane whose
+// offset is kOffMasked lies outside the range: its load returns zeros and its
+// store is dropped. The range is capped below 2^31 so that holds for any tensor.
+// The range check covers the per-lane offset only (the scalar offset is excluded),
+// so every lane that must not touch memory gets kOffMasked explicitly.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+constexpr uint32_t kOffMasked = 0x80000000u;
+constexpr int kRawBufferFlags = 0x00020000;   // 32-bit data format, raw addressing
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    const int64_t b = bytes < 0 ? 0 : (bytes > 0x7ffffff0 ? 0x7ffffff0 : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)b, kRawBufferFlags);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 buf_load16f(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+}
+__device__ __forceinline__ void buf_store16(uint4 v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{v.x, v.y, v.z, v.w}, r, (int)voff, (int)soff, 0);
+}
 
 // Eight consecutive elements of a row: load/store as fp32 values, plus the raw
 // packed bf16 words (the MFMA operand) when the element type is bf16.
@@ -274,15 +308,22 @@ __global__ __launch_bounds__(kEwBlock) void post_kernel(const void* __restrict__
 // of all 4 streams. The step's slice of hc_fn (24 rows x 4 streams x 32 channels)
 // is staged in LDS once per workgroup and shared by its 4 waves.
 //
-// Projection engines:
-//   VALU  fp32 LDS copy of the slice; each lane accumulates 24 dot products
-//         over its 32 values, then the 4 lane groups are summed with shuffles.
-//   MFMA  (bf16 streams) the bf16 stream values are exact MFMA A operands; the
-//         fp32 weights are split into three bf16 terms (hi + mid + lo, ~24
-//         significant bits) stored in the B-operand layout of
-//         v_mfma_f32_16x16x32_bf16; 24 mixes use two 16-wide column tiles
-//         (rows 24..31 zero). Each term accumulates into the same fp32
-//         accumulator.
+// Projection engines (A = 16 tokens x k, B = k x 16 mixes, fp32 accumulators;
+// the 24 mixes use two 16-wide column tiles whose columns 24..31 are zero):
+//   bf16 streams: v_mfma_f32_16x16x32_bf16. The bf16 stream values are exact A
+//         operands; the fp32 weights are split into three bf16 terms (hi + mid +
+//         lo, ~24 significant bits), each accumulated into the same accumulator.
+//   fp32 streams: v_mfma_f32_16x16x4f32 with the fp32 values and weights as they
+//         are; k runs over the 4 lane groups, one MFMA per (stream, channel).
+//
+// Pipelining: while step ci is computed, the stream values of step ci+1 are
+// already loaded into registers and its weights fetched; the weights are split
+// into the other LDS buffer after step ci's MFMAs, then one barrier per step.
+//
+// Grid: one dimension, workgroup L -> (tile = L / nsplit, slice = L % nsplit).
+// Workgroups are dealt to the 8 XCDs round-robin, so with nsplit a multiple of 8
+// every XCD works on a fixed set of channel slices and its L2 holds only that
+// part of hc_fn.
 struct PassArgs {
     const void* res;
     const void* f;
@@ -297,39 +338,69 @@ struct PassArgs {
     int64_t d;
     int nchunks;
     int chunks_per_split;
+    int nsplit;
 };
 
 constexpr int kPassBlock = kWaves * 64;
-constexpr int kMfmaStage = 3 * 2 * kHC * 64;   // uint4 per LDS buffer: term x ntile x stream x lane
-constexpr int kValuStage = kMix * kHC * kChunk; // floats per LDS buffer
+constexpr int kBf16Stage = 3 * 2 * kHC * 64;   // uint4 per LDS buffer: term x ntile x stream x lane
+constexpr int kF32Row = kHC * kChunk + 4;      // floats per mix row of the fp32 stage (padded)
+constexpr int kF32Stage = 32 * kF32Row;        // floats per LDS buffer: 32 mix rows (24..31 zero)
+constexpr int kStageLoads = (kMix * kHC * kChunk / 4) / kPassBlock;  // float4 per thread per step
 
-template <bool kMfma>
+// B-fragment slot (16 B) of (term, ntile, stream j, lane) in a bf16 weight stage,
+// XOR-swizzled within groups of 8 so that the split's 8-byte writes spread over
+// all banks while the MFMA's lane-ordered 16-byte reads stay conflict-free.
+// Columns 8..15 of a slot group stay in 8..15 (padding maps onto padding).
+__device__ __forceinline__ int b_slot(int term, int nt, int j, int lane) {
+    const int slot = ((term * 2 + nt) * 4 + j) * 64 + lane;
+    return slot ^ (((lane >> 4) + 4 * (j & 1)) & 7);
+}
+
+template <bool kBf16>
 struct PassLds;
 template <>
 struct PassLds<true> {
-    uint4 b[2][kMfmaStage];
+    uint4 b[2][kBf16Stage];
 };
 template <>
 struct PassLds<false> {
-    float w[2][kValuStage];
+    float w[2][kF32Stage];
 };
 
-// Stage hc_fn[i][j*d + ci*32 + 0..31] for i < 24, j < 4 into LDS buffer `buf`.
-template <bool kMfma>
-__device__ __forceinline__ void stage_weights(PassLds<kMfma>& lds, int buf, const float* __restrict__ W,
+__device__ __forceinline__ uint4* lds_b(PassLds<true>& l, int buf) { return l.b[buf]; }
+__device__ __forceinline__ uint4* lds_b(PassLds<false>&, int) { return nullptr; }
+__device__ __forceinline__ float* lds_w(PassLds<false>& l, int buf) { return l.w[buf]; }
+__device__ __forceinline__ float* lds_w(PassLds<true>&, int) { return nullptr; }
+
+// Thread's share of hc_fn[i][j*d + ci*32 + 0..31] (i < 24, j < 4): kStageLoads
+// float4 values; entry q covers idx = threadIdx.x + q*256 -> i = idx/32,
+// j = (idx/8)%4, 4 channels at (idx%8)*4. Channels past d read as zero: the load
+// itself always targets an in-bounds address (clamped) and the value is masked,
+// so no load sits behind a branch.
+__device__ __forceinline__ void fetch_weights(float4 (&w)[kStageLoads], const float* __restrict__ W,
                                               int64_t d, int ci) {
     const int64_t D = d * kHC;
 #pragma unroll
-    for (int q = 0; q < (kMix * kHC * kChunk / 4) / kPassBlock; ++q) {
-        const int idx = threadIdx.x + q * kPassBlock;   // 0 .. 767
-        const int i = idx >> 5;                         // mix row
-        const int j = (idx >> 3) & 3;                   // stream
-        const int c4 = idx & 7;                         // float4 within the 32 channels
+    for (int q = 0; q < kStageLoads; ++q) {
+        const int idx = threadIdx.x + q * kPassBlock;
+        const int i = idx >> 5, j = (idx >> 3) & 3, c4 = idx & 7;
         const int64_t e = (int64_t)ci * kChunk + c4 * 4;
-        float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (e < d) w = *reinterpret_cast<const float4*>(W + i * D + j * d + e);
-        if constexpr (kMfma) {
-            const float wv[4] = {w.x, w.y, w.z, w.w};
+        const bool ok = e < d;
+        const float4 v = *reinterpret_cast<const float4*>(W + i * D + j * d + (ok ? e : 0));
+        w[q] = ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+}
+
+// Splits (bf16) or copies (fp32) the fetched weights into LDS stage buffer `dst`
+// (one buffer: kBf16Stage uint4 or kF32Stage floats).
+template <bool kBf16>
+__device__ __forceinline__ void commit_weights(void* dst, const float4 (&w)[kStageLoads]) {
+#pragma unroll
+    for (int q = 0; q < kStageLoads; ++q) {
+        const int idx = threadIdx.x + q * kPassBlock;
+        const int i = idx >> 5, j = (idx >> 3) & 3, c4 = idx & 7;
+        if constexpr (kBf16) {
+            const float wv[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
             uint32_t hi[2], mid[2], lo[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -340,219 +411,596 @@ __device__ __forceinline__ void stage_weights(PassLds<kMfma>& lds, int buf, cons
                 const float sa = ra - bf16_lo(mid[h]), sb = rb - bf16_hi(mid[h]);
                 lo[h] = pack_bf16x2(sa, sb);
             }
+            // B operand of tile nt = i/16: lane (k-group = c4/2)*16 + column i%16,
+            // 8 bf16 per lane of which this float4 fills half c4%2
             const int nt = i >> 4, col = i & 15;
             const int lane = (c4 >> 1) * 16 + col;
             const int half = c4 & 1;
-            uint2* base = reinterpret_cast<uint2*>(lds.b[buf]);
-            base[(((0 * 2 + nt) * kHC + j) * 64 + lane) * 2 + half] = make_uint2(hi[0], hi[1]);
-            base[(((1 * 2 + nt) * kHC + j) * 64 + lane) * 2 + half] = make_uint2(mid[0], mid[1]);
-            base[(((2 * 2 + nt) * kHC + j) * 64 + lane) * 2 + half] = make_uint2(lo[0], lo[1]);
+            uint2* base = reinterpret_cast<uint2*>(dst);
+            base[b_slot(0, nt, j, lane) * 2 + half] = make_uint2(hi[0], hi[1]);
+            base[b_slot(1, nt, j, lane) * 2 + half] = make_uint2(mid[0], mid[1]);
+            base[b_slot(2, nt, j, lane) * 2 + half] = make_uint2(lo[0], lo[1]);
         } else {
-            reinterpret_cast<float4*>(lds.w[buf])[idx] = w;  // layout [i][j][32]
+            // layout [32 rows][4 streams][32 channels], row stride kF32Row floats
+            *reinterpret_cast<float4*>(static_cast<float*>(dst) + i * kF32Row + j * kChunk + c4 * 4) = w[q];
         }
     }
 }
 
-template <bool kBf16, bool kPost, bool kPre, bool kMfma>
+// Raw 8-element stream data of one lane for one step (registers only).
+template <bool kBf16>
+struct Raw8;
+template <>
+struct Raw8<true> {
+    uint4 w;
+    __device__ __forceinline__ void load(const void* base, int64_t idx) {
+        w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
+    }
+    __device__ __forceinline__ void zero() { w = make_uint4(0, 0, 0, 0); }
+    __device__ __forceinline__ void to(Vec8<true>& v) const {
+        v.raw = w;
+        v.unpack();
+    }
+};
+template <>
+struct Raw8<false> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const void* base, int64_t idx) {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+        a = p[0];
+        b = p[1];
+    }
+    __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
+    __device__ __forceinline__ void to(Vec8<false>& v) const {
+        v.v[0] = a.x; v.v[1] = a.y; v.v[2] = a.z; v.v[3] = a.w;
+        v.v[4] = b.x; v.v[5] = b.y; v.v[6] = b.z; v.v[7] = b.w;
+    }
+};
+
+template <bool kBf16, bool kPost>
+struct StepData {
+    Raw8<kBf16> x[kHC];
+    Raw8<kBf16> f;  // used when kPost
+};
+
+// Loads one step's stream values of a lane. Out-of-range lanes (token >= n or
+// channel >= d) load from token 0 / channel 0, which always exists, and get
+// zeros, so the loads are unconditional.
+template <bool kBf16, bool kPost>
+__device__ __forceinline__ void load_step(StepData<kBf16, kPost>& s, const PassArgs& a, int64_t t, bool live,
+                                          int64_t e) {
+    const int64_t tt = live ? t : 0, ee = live ? e : 0;
+#pragma unroll
+    for (int j = 0; j < kHC; ++j) s.x[j].load(a.res, (tt * kHC + j) * a.d + ee);
+    if constexpr (kPost) s.f.load(a.f, tt * a.d + ee);
+    if (!live) {
+#pragma unroll
+        for (int j = 0; j < kHC; ++j) s.x[j].zero();
+        if constexpr (kPost) s.f.zero();
+    }
+}
+
+// Per-lane constant state of one sweep (one 16-token tile).
+struct LaneCoef {
+    float pk[kHC];        // previous sublayer's post (expand)
+    float cm[kHC * kHC];  // previous sublayer's comb (expand)
+    float pim[kHC];       // collapse weights
+};
+
+template <bool kPost, bool kPre>
+__device__ __forceinline__ void load_coef(LaneCoef& co, const PassArgs& a, int64_t t, bool tok_ok) {
+#pragma unroll
+    for (int j = 0; j < kHC; ++j) co.pk[j] = co.pim[j] = 0.f;
+#pragma unroll
+    for (int i = 0; i < kHC * kHC; ++i) co.cm[i] = 0.f;
+    if (!tok_ok) return;
+    if constexpr (kPost) {
+        const float4 pv = reinterpret_cast<const float4*>(a.post_prev)[t];
+        co.pk[0] = pv.x; co.pk[1] = pv.y; co.pk[2] = pv.z; co.pk[3] = pv.w;
+#pragma unroll
+        for (int j = 0; j < kHC; ++j) {
+            const float4 c = reinterpret_cast<const float4*>(a.comb_prev)[t * 4 + j];
+            co.cm[4 * j] = c.x; co.cm[4 * j + 1] = c.y; co.cm[4 * j + 2] = c.z; co.cm[4 * j + 3] = c.w;
+        }
+    }
+    if constexpr (kPre) {
+        const float4 pv = reinterpret_cast<const float4*>(a.pre_mix)[t];
+        co.pim[0] = pv.x; co.pim[1] = pv.y; co.pim[2] = pv.z; co.pim[3] = pv.w;
+    }
+}
+
+// Elementwise part of one step for one tile: expand (optional), collapse
+// (optional), sum of squares. Leaves the (rounded) stream values in xs.
+template <bool kBf16, bool kPost, bool kPre>
+__device__ __forceinline__ void step_elementwise(const PassArgs& a, const StepData<kBf16, kPost>& in,
+                                                 const LaneCoef& co, int64_t t, bool live, int64_t e,
+                                                 Vec8<kBf16> (&xs)[kHC], float& sumsq) {
+    const int64_t d = a.d;
+#pragma unroll
+    for (int j = 0; j < kHC; ++j) in.x[j].to(xs[j]);
+    if constexpr (kPost) {
+        Vec8<kBf16> fv, x1[kHC];
+        in.f.to(fv);
+        expand8<kBf16>(fv, xs, co.pk, co.cm, x1);
+#pragma unroll
+        for (int k = 0; k < kHC; ++k) {
+            if (live) x1[k].store(a.streams_out, (t * kHC + k) * d + e);
+            xs[k] = x1[k];
+        }
+    }
+    if constexpr (kPre) {
+        Vec8<kBf16> yv;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            float s = 0.f;
+#pragma unroll
+            for (int j = 0; j < kHC; ++j) s = fmaf(co.pim[j], xs[j].v[c], s);
+            yv.v[c] = s;
+        }
+        yv.round();
+        if (live) yv.store(a.y, t * d + e);
+    }
+#pragma unroll
+    for (int j = 0; j < kHC; ++j)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) sumsq = fmaf(xs[j].v[c], xs[j].v[c], sumsq);
+}
+
+// The sweep: workgroup = 4 waves x kTiles tiles of 16 tokens. Per 32-channel step,
+// each lane loads its tiles' stream values, fetches the next step's weights (L2)
+// before doing the step's work, and after the step's MFMAs splits those weights
+// into the other LDS buffer; one barrier per step. Every B fragment read from LDS
+// feeds all kTiles tiles of the wave.
+template <bool kBf16, bool kPost, bool kPre>
 __global__ __launch_bounds__(kPassBlock) void pass_kernel(PassArgs a) {
-    static_assert(!kMfma || kBf16, "the MFMA engine needs bf16 stream values");
-    __shared__ PassLds<kMfma> lds;
+    __shared__ PassLds<kBf16> lds;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int r = lane & 15;
     const int g = lane >> 4;
     const int64_t n = a.n, d = a.d;
-    const int64_t t = (int64_t)blockIdx.x * kTokWG + wave * kTokWave + r;
-    const bool tok_ok = t < n;
-    const int split = blockIdx.y;
+    const int split = (int)(blockIdx.x % (unsigned)a.nsplit);
+    const int64_t group = blockIdx.x / (unsigned)a.nsplit;
+    const int64_t tbase = group * kTokWG + wave * kTokWave;   // first token of the wave
     const int c_begin = split * a.chunks_per_split;
     const int c_end = min(a.nchunks, c_begin + a.chunks_per_split);
 
-    if constexpr (kMfma) {
-        // the B rows 24..31 (tile 1, columns 8..15) stay zero for the whole sweep
+    // the B columns 24..31 (tile 1, columns 8..15) stay zero for the whole sweep
+    if constexpr (kBf16) {
         for (int z = threadIdx.x; z < 2 * 3 * kHC * 4 * 8; z += kPassBlock) {
             const int col = 8 + (z & 7), gg = (z >> 3) & 3, j = (z >> 5) & 3, term = (z >> 7) % 3,
                       buf = z / (3 * kHC * 4 * 8);
-            lds.b[buf][((term * 2 + 1) * kHC + j) * 64 + gg * 16 + col] = make_uint4(0, 0, 0, 0);
+            lds.b[buf][b_slot(term, 1, j, gg * 16 + col)] = make_uint4(0, 0, 0, 0);
+        }
+    } else {
+        for (int z = threadIdx.x; z < 2 * 8 * kF32Row; z += kPassBlock) {
+            const int buf = z / (8 * kF32Row), o = z - buf * 8 * kF32Row;
+            lds.w[buf][kMix * kF32Row + o] = 0.f;
         }
     }
 
-    float pk[kHC] = {0.f, 0.f, 0.f, 0.f}, cm[kHC * kHC], pim[kHC] = {0.f, 0.f, 0.f, 0.f};
+    int64_t t[kTiles];
+    bool tok_ok[kTiles];
+    LaneCoef co[kTiles];
+    floatx4_t acc[kTiles][2];
+    float sumsq[kTiles];
 #pragma unroll
-    for (int i = 0; i < kHC * kHC; ++i) cm[i] = 0.f;
-    if (tok_ok) {
-        if constexpr (kPost) {
-            const float4 pv = reinterpret_cast<const float4*>(a.post_prev)[t];
-            pk[0] = pv.x; pk[1] = pv.y; pk[2] = pv.z; pk[3] = pv.w;
-#pragma unroll
-            for (int j = 0; j < kHC; ++j) {
-                const float4 c = reinterpret_cast<const float4*>(a.comb_prev)[t * 4 + j];
-                cm[4 * j] = c.x; cm[4 * j + 1] = c.y; cm[4 * j + 2] = c.z; cm[4 * j + 3] = c.w;
-            }
-        }
-        if constexpr (kPre) {
-            const float4 pv = reinterpret_cast<const float4*>(a.pre_mix)[t];
-            pim[0] = pv.x; pim[1] = pv.y; pim[2] = pv.z; pim[3] = pv.w;
-        }
+    for (int q = 0; q < kTiles; ++q) {
+        t[q] = tbase + q * 16 + r;
+        tok_ok[q] = t[q] < n;
+        load_coef<kPost, kPre>(co[q], a, t[q], tok_ok[q]);
+        acc[q][0] = acc[q][1] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        sumsq[q] = 0.f;
     }
 
-    floatx4_t acc_m[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    float acc_v[kMix];
-#pragma unroll
-    for (int i = 0; i < kMix; ++i) acc_v[i] = 0.f;
-    float sumsq = 0.f;
-
-    if (c_begin < c_end) stage_weights<kMfma>(lds, 0, a.hc_fn, d, c_begin);
+    if (c_begin < c_end) {
+        float4 w0[kStageLoads];
+        fetch_weights(w0, a.hc_fn, d, c_begin);
+        commit_weights<kBf16>(kBf16 ? (void*)lds_b(lds, 0) : (void*)lds_w(lds, 0), w0);
+    }
     __syncthreads();
 
     for (int ci = c_begin; ci < c_end; ++ci) {
         const int buf = (ci - c_begin) & 1;
-        if (ci + 1 < c_end) stage_weights<kMfma>(lds, buf ^ 1, a.hc_fn, d, ci + 1);
-
+        const bool more = ci + 1 < c_end;
+        float4 wnext[kStageLoads];
+        if (more) fetch_weights(wnext, a.hc_fn, d, ci + 1);   // L2, committed after the MFMAs
         const int64_t e = (int64_t)ci * kChunk + g * 8;
-        const bool live = tok_ok && e < d;
-        Vec8<kBf16> xs[kHC];
-        if (live) {
+        StepData<kBf16, kPost> in[kTiles];
 #pragma unroll
-            for (int j = 0; j < kHC; ++j) xs[j].load(a.res, (t * kHC + j) * d + e);
-        } else {
-#pragma unroll
-            for (int j = 0; j < kHC; ++j) xs[j].zero();
-        }
-        if constexpr (kPost) {
-            Vec8<kBf16> fv, x1[kHC];
-            if (live) fv.load(a.f, t * d + e);
-            else fv.zero();
-            expand8<kBf16>(fv, xs, pk, cm, x1);
-#pragma unroll
-            for (int k = 0; k < kHC; ++k) {
-                if (live) x1[k].store(a.streams_out, (t * kHC + k) * d + e);
-                xs[k] = x1[k];
-            }
-        }
-        if constexpr (kPre) {
-            Vec8<kBf16> yv;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                float s = 0.f;
-#pragma unroll
-                for (int j = 0; j < kHC; ++j) s = fmaf(pim[j], xs[j].v[c], s);
-                yv.v[c] = s;
-            }
-            yv.round();
-            if (live) yv.store(a.y, t * d + e);
-        }
-#pragma unroll
-        for (int j = 0; j < kHC; ++j)
-#pragma unroll
-            for (int c = 0; c < 8; ++c) sumsq = fmaf(xs[j].v[c], xs[j].v[c], sumsq);
+        for (int q = 0; q < kTiles; ++q) load_step<kBf16, kPost>(in[q], a, t[q], tok_ok[q] && e < d, e);
 
-        if constexpr (kMfma) {
+        Vec8<kBf16> xs[kTiles][kHC];
+#pragma unroll
+        for (int q = 0; q < kTiles; ++q)
+            step_elementwise<kBf16, kPost, kPre>(a, in[q], co[q], t[q], tok_ok[q] && e < d, e, xs[q], sumsq[q]);
+
+        if constexpr (kBf16) {
             const uint4* B = lds.b[buf];
 #pragma unroll
-            for (int j = 0; j < kHC; ++j) {
-                const bf16x8_t A = __builtin_bit_cast(bf16x8_t, xs[j].raw);
+            for (int j = 0; j < kHC; ++j)
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
                     for (int term = 0; term < 3; ++term) {
-                        const bf16x8_t Bv =
-                            __builtin_bit_cast(bf16x8_t, B[((term * 2 + nt) * kHC + j) * 64 + lane]);
-                        acc_m[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bv, acc_m[nt], 0, 0, 0);
-                    }
-            }
-        } else {
-            const float4* W = reinterpret_cast<const float4*>(lds.w[buf]);
+                        const bf16x8_t Bv = __builtin_bit_cast(bf16x8_t, B[b_slot(term, nt, j, lane)]);
 #pragma unroll
-            for (int i = 0; i < kMix; ++i) {
-                float s = acc_v[i];
+                        for (int q = 0; q < kTiles; ++q)
+                            acc[q][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8_t, xs[q][j].raw), Bv, acc[q][nt], 0, 0, 0);
+                    }
+        } else {
+            // lane (r, g): A = token r, channel g*8 + c; B = mix nt*16 + r, same channel
+            const float* W = lds.w[buf];
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
                 for (int j = 0; j < kHC; ++j) {
-                    const float4 w0 = W[((i * kHC + j) * kChunk + g * 8) / 4];
-                    const float4 w1 = W[((i * kHC + j) * kChunk + g * 8) / 4 + 1];
-                    s = fmaf(w0.x, xs[j].v[0], s); s = fmaf(w0.y, xs[j].v[1], s);
-                    s = fmaf(w0.z, xs[j].v[2], s); s = fmaf(w0.w, xs[j].v[3], s);
-                    s = fmaf(w1.x, xs[j].v[4], s); s = fmaf(w1.y, xs[j].v[5], s);
-                    s = fmaf(w1.z, xs[j].v[6], s); s = fmaf(w1.w, xs[j].v[7], s);
+                    const float* wr = W + (nt * 16 + r) * kF32Row + j * kChunk + g * 8;
+                    const float4 b0 = *reinterpret_cast<const float4*>(wr);
+                    const float4 b1 = *reinterpret_cast<const float4*>(wr + 4);
+                    const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+                    for (int c = 0; c < 8; ++c)
+#pragma unroll
+                        for (int q = 0; q < kTiles; ++q)
+                            acc[q][nt] =
+                                __builtin_amdgcn_mfma_f32_16x16x4f32(xs[q][j].v[c], bv[c], acc[q][nt], 0, 0, 0);
                 }
-                acc_v[i] = s;
-            }
         }
+        // the other buffer was last read before the previous barrier
+        if (more) commit_weights<kBf16>(kBf16 ? (void*)lds_b(lds, buf ^ 1) : (void*)lds_w(lds, buf ^ 1), wnext);
         __syncthreads();
     }
 
-    // partial results of this (token tile, channel slice)
+    // partial results of this (token group, channel slice)
     float* part = a.part + (int64_t)split * n * kPart;
-    sumsq += __shfl_xor(sumsq, 16);
-    sumsq += __shfl_xor(sumsq, 32);
-    if (g == 0 && tok_ok) part[t * kPart + kMix] = sumsq;
-    if constexpr (kMfma) {
+#pragma unroll
+    for (int q = 0; q < kTiles; ++q) {
+        float s = sumsq[q];
+        s += __shfl_xor(s, 16);
+        s += __shfl_xor(s, 32);
+        if (g == 0 && tok_ok[q]) part[t[q] * kPart + kMix] = s;
         // accumulator layout: lane holds rows 4*g .. 4*g+3 (tokens), column r (mix)
-        const int64_t t0 = (int64_t)blockIdx.x * kTokWG + wave * kTokWave + 4 * g;
+        const int64_t t0 = tbase + q * 16 + 4 * g;
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             const int mix = nt * 16 + r;
             if (mix < kMix) {
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii)
-                    if (t0 + ii < n) part[(t0 + ii) * kPart + mix] = acc_m[nt][ii];
+                    if (t0 + ii < n) part[(t0 + ii) * kPart + mix] = acc[q][nt][ii];
             }
         }
-    } else {
-#pragma unroll
-        for (int i = 0; i < kMix; ++i) {
-            float s = acc_v[i];
-            s += __shfl_xor(s, 16);
-            s += __shfl_xor(s, 32);
-            acc_v[i] = s;
+    }
+}
+
+// ------------------------------------------------------- bf16 sweep (rowwise)
+// The MFMA operand layout puts 16 tokens x 64 B in one load instruction, which
+// leaves every cache line half used per request; measured on MI355X such loads
+// stream at <= 3.9 TB/s while 256-byte row runs reach ~5.8 TB/s. So the bf16
+// sweep loads rowwise and transposes through LDS:
+//   - super-step = 128 channels. Lane (sub = lane/16, ch = lane%16) of wave w
+//     loads, for token group G (4 per wave) and stream j, 16 B at token
+//     tbase + 4G + sub, channels cs + 8ch: one instruction = 4 tokens x 256 B.
+//   - expand / collapse / sum of squares run in that layout (stores are 256 B
+//     runs too); the rounded values are then written, one 32-channel k-block at
+//     a time, into the wave's own LDS tile in MFMA A layout (row = token 4G+sub,
+//     k-group = ch%4), XOR-swizzled so both the writes and the reads are free of
+//     bank conflicts, and read back as A operands.
+//   - weights: the same LDS stage per k-block as the generic sweep (three bf16
+//     terms in B layout, double-buffered, one barrier per k-block).
+constexpr int kSuper = 128;              // channels per super-step
+constexpr int kKbPerSuper = kSuper / kChunk;
+constexpr int kCoefF4 = 6;               // float4 per token: post_prev, comb_prev x4, pre_mix
+
+struct SweepLds {
+    uint4 b[2][kBf16Stage];              // weight stage, 2 x 24 KB
+    uint4 a[kWaves][kHC * 64];           // per-wave A tile of one k-block, 4 x 4 KB
+    float4 coef[kTokWG][kCoefF4];        // per-token coefficients, 6 KB
+};
+
+__device__ __forceinline__ int a_slot(int slot) { return slot ^ ((slot >> 4) & 7); }
+
+template <bool kPost, bool kPre>
+__global__ __launch_bounds__(kPassBlock) void sweep_bf16_kernel(PassArgs a) {
+    static_assert(kTokWave == 16, "the rowwise sweep uses one 16-token tile per wave");
+    __shared__ SweepLds lds;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // scalar: uniform bases
+    const int sub = lane >> 4, ch = lane & 15;   // rowwise role
+    const int r = lane & 15, g = lane >> 4;      // MFMA role
+    const int64_t n = a.n, d = a.d;
+    const int split = (int)(blockIdx.x % (unsigned)a.nsplit);
+    const int64_t group = blockIdx.x / (unsigned)a.nsplit;
+    const int64_t tbase = group * kTokWG + wave * kTokWave;
+    // this workgroup's 32-channel k-blocks [kb_begin, kb_end), whole super-steps
+    const int nkb = a.nchunks;
+    const int kb_begin = split * a.chunks_per_split;
+    const int kb_end = min(nkb, kb_begin + a.chunks_per_split);
+
+    // zero B columns 24..31; per-token coefficients of the workgroup into LDS
+    for (int z = threadIdx.x; z < 2 * 3 * kHC * 4 * 8; z += kPassBlock) {
+        const int col = 8 + (z & 7), gg = (z >> 3) & 3, j = (z >> 5) & 3, term = (z >> 7) % 3,
+                  buf = z / (3 * kHC * 4 * 8);
+        lds.b[buf][b_slot(term, 1, j, gg * 16 + col)] = make_uint4(0, 0, 0, 0);
+    }
+    for (int z = threadIdx.x; z < kTokWG * kCoefF4; z += kPassBlock) {
+        const int tl = z / kCoefF4, q = z - tl * kCoefF4;
+        const int64_t tt = group * kTokWG + tl;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (tt < n) {
+            if (kPost && q == 0) v = reinterpret_cast<const float4*>(a.post_prev)[tt];
+            if (kPost && q >= 1 && q <= 4) v = reinterpret_cast<const float4*>(a.comb_prev)[tt * 4 + q - 1];
+            if (kPre && q == 5) v = reinterpret_cast<const float4*>(a.pre_mix)[tt];
         }
-        if (g == 0 && tok_ok) {
-            float4* dst = reinterpret_cast<float4*>(part + t * kPart);
+        lds.coef[tl][q] = v;
+    }
+
+    floatx4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    float sumsq[4] = {0.f, 0.f, 0.f, 0.f};
+
+    // buffer resources based at the wave's first token; ranges end at token n
+    const int64_t row_x = kHC * d * 2, row_f = d * 2;   // bytes per token
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(static_cast<const char*>(a.res) + tbase * row_x, (n - tbase) * row_x);
+    const __amdgpu_buffer_rsrc_t rf = make_rsrc(kPost ? static_cast<const char*>(a.f) + tbase * row_f : nullptr,
+                                                kPost ? (n - tbase) * row_f : 0);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(kPost ? static_cast<char*>(a.streams_out) + tbase * row_x : nullptr,
+                                                kPost ? (n - tbase) * row_x : 0);
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(kPre ? static_cast<char*>(a.y) + tbase * row_f : nullptr,
+                                                kPre ? (n - tbase) * row_f : 0);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.hc_fn, (int64_t)kMix * kHC * d * 4);
+    // per-lane offsets (token sub of each group, channel 8*ch); groups, streams and
+    // the super-step go into the scalar offset
+    const uint32_t lane_x = (uint32_t)(sub * row_x + ch * 16);
+    const uint32_t lane_f = (uint32_t)(sub * row_f + ch * 16);
+    // weight fetch offsets of this thread: hc_fn[i][j*d + 4*c4] for idx = tid + q*256
+    uint32_t lane_w[kStageLoads];
+    int c4w[kStageLoads];
 #pragma unroll
-            for (int q = 0; q < kMix / 4; ++q)
-                dst[q] = make_float4(acc_v[4 * q], acc_v[4 * q + 1], acc_v[4 * q + 2], acc_v[4 * q + 3]);
+    for (int q = 0; q < kStageLoads; ++q) {
+        const int idx = threadIdx.x + q * kPassBlock;
+        const int i = idx >> 5, j = (idx >> 3) & 3;
+        c4w[q] = idx & 7;
+        lane_w[q] = (uint32_t)(((int64_t)i * kHC * d + (int64_t)j * d + c4w[q] * 4) * 4);
+    }
+    auto fetch_w = [&](float4 (&w)[kStageLoads], int ci) {
+#pragma unroll
+        for (int q = 0; q < kStageLoads; ++q) {
+            const bool ok = (int64_t)ci * kChunk + c4w[q] * 4 < d;
+            w[q] = buf_load16f(rw, ok ? lane_w[q] : kOffMasked, (uint32_t)(ci * kChunk * 4));
+        }
+    };
+
+    if (kb_begin < kb_end) {
+        float4 w0[kStageLoads];
+        fetch_w(w0, kb_begin);
+        commit_weights<true>(lds.b[0], w0);
+    }
+    __syncthreads();
+
+    int buf = 0;
+    for (int kb0 = kb_begin; kb0 < kb_end; kb0 += kKbPerSuper) {
+        const int64_t cs = (int64_t)kb0 * kChunk;     // first channel of the super-step
+        const int64_t c = cs + ch * 8;
+        const bool c_ok = c < d && c < (int64_t)kb_end * kChunk;
+        // lanes past token n or channel d are masked
+        uint32_t vx[4], vf[4];
+#pragma unroll
+        for (int G = 0; G < 4; ++G) {
+            const bool live = c_ok && tbase + 4 * G + sub < n;
+            vx[G] = live ? lane_x : kOffMasked;
+            vf[G] = live ? lane_f : kOffMasked;
+        }
+        Raw8<true> X[4][kHC], F[4];
+#pragma unroll
+        for (int G = 0; G < 4; ++G) {
+#pragma unroll
+            for (int j = 0; j < kHC; ++j)
+                X[G][j].w = buf_load16(rx, vx[G], (uint32_t)((4 * G * kHC + j) * row_f + cs * 2));
+            if constexpr (kPost) F[G].w = buf_load16(rf, vf[G], (uint32_t)(4 * G * row_f + cs * 2));
+        }
+        // expand / collapse / sum of squares, rowwise, two channels (one packed
+        // word per stream) at a time; the rounded streams go back into X
+#pragma unroll
+        for (int G = 0; G < 4; ++G) {
+            const float4* cf = lds.coef[wave * kTokWave + 4 * G + sub];
+            float pk[kHC], cm[kHC * kHC], pim[kHC];
+            if constexpr (kPost) {
+                const float4 pv = cf[0];
+                pk[0] = pv.x; pk[1] = pv.y; pk[2] = pv.z; pk[3] = pv.w;
+#pragma unroll
+                for (int j = 0; j < kHC; ++j) {
+                    const float4 cv = cf[1 + j];
+                    cm[4 * j] = cv.x; cm[4 * j + 1] = cv.y; cm[4 * j + 2] = cv.z; cm[4 * j + 3] = cv.w;
+                }
+            }
+            if constexpr (kPre) {
+                const float4 pv = cf[5];
+                pim[0] = pv.x; pim[1] = pv.y; pim[2] = pv.z; pim[3] = pv.w;
+            }
+            uint32_t yw[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                uint32_t xw[kHC];
+#pragma unroll
+                for (int j = 0; j < kHC; ++j) xw[j] = (&X[G][j].w.x)[w];
+                if constexpr (kPost) {
+                    const uint32_t fw = (&F[G].w.x)[w];
+                    const float f0 = bf16_lo(fw), f1 = bf16_hi(fw);
+                    uint32_t ow[kHC];
+#pragma unroll
+                    for (int k = 0; k < kHC; ++k) {
+                        float o0 = pk[k] * f0, o1 = pk[k] * f1;
+#pragma unroll
+                        for (int j = 0; j < kHC; ++j) {
+                            o0 = fmaf(cm[4 * j + k], bf16_lo(xw[j]), o0);
+                            o1 = fmaf(cm[4 * j + k], bf16_hi(xw[j]), o1);
+                        }
+                        ow[k] = pack_bf16x2(o0, o1);
+                    }
+#pragma unroll
+                    for (int k = 0; k < kHC; ++k) xw[k] = (&X[G][k].w.x)[w] = ow[k];
+                }
+                float y0 = 0.f, y1 = 0.f;
+#pragma unroll
+                for (int j = 0; j < kHC; ++j) {
+                    const float v0 = bf16_lo(xw[j]), v1 = bf16_hi(xw[j]);
+                    if constexpr (kPre) {
+                        y0 = fmaf(pim[j], v0, y0);
+                        y1 = fmaf(pim[j], v1, y1);
+                    }
+                    sumsq[G] = fmaf(v0, v0, sumsq[G]);
+                    sumsq[G] = fmaf(v1, v1, sumsq[G]);
+                }
+                yw[w] = pack_bf16x2(y0, y1);
+            }
+            if constexpr (kPost) {
+#pragma unroll
+                for (int k = 0; k < kHC; ++k)
+                    buf_store16(X[G][k].w, ro, vx[G], (uint32_t)((4 * G * kHC + k) * row_f + cs * 2));
+            }
+            if constexpr (kPre)
+                buf_store16(make_uint4(yw[0], yw[1], yw[2], yw[3]), ry, vf[G], (uint32_t)(4 * G * row_f + cs * 2));
+            // keep the sum of squares here: otherwise it is sunk past the k-block loop
+            // and the unpacked values of all groups stay live across it
+            asm volatile("" : "+v"(sumsq[G]));
+            __builtin_amdgcn_sched_barrier(0);   // one token group's temporaries at a time
+        }
+        // projection, one k-block at a time (kept rolled: bounded register lifetimes)
+#pragma unroll 1
+        for (int k = 0; k < kKbPerSuper; ++k) {
+            const int ci = kb0 + k;
+            if (ci >= kb_end) break;                   // uniform across the workgroup
+            const bool more = ci + 1 < kb_end;
+            float4 wnext[kStageLoads];
+            if (more) fetch_w(wnext, ci + 1);
+            uint4* at = lds.a[wave];
+            if ((ch >> 2) == k) {
+#pragma unroll
+                for (int G = 0; G < 4; ++G)
+#pragma unroll
+                    for (int j = 0; j < kHC; ++j) at[a_slot(j * 64 + (ch & 3) * 16 + 4 * G + sub)] = X[G][j].w;
+            }
+            const uint4* B = lds.b[buf];
+#pragma unroll
+            for (int j = 0; j < kHC; ++j) {
+                const bf16x8_t A = __builtin_bit_cast(bf16x8_t, at[a_slot(j * 64 + lane)]);
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                    for (int term = 0; term < 3; ++term) {
+                        const bf16x8_t Bv = __builtin_bit_cast(bf16x8_t, B[b_slot(term, nt, j, lane)]);
+                        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bv, acc[nt], 0, 0, 0);
+                    }
+                __builtin_amdgcn_sched_barrier(0);   // one stream's 6 B fragments live at a time
+            }
+            if (more) commit_weights<true>(lds.b[buf ^ 1], wnext);
+            __syncthreads();
+            buf ^= 1;
+        }
+    }
+
+    // partial results of this (token group, channel slice)
+    float* part = a.part + (int64_t)split * n * kPart;
+#pragma unroll
+    for (int G = 0; G < 4; ++G) {
+        float s = sumsq[G];
+        s += __shfl_xor(s, 1);
+        s += __shfl_xor(s, 2);
+        s += __shfl_xor(s, 4);
+        s += __shfl_xor(s, 8);
+        const int64_t t = tbase + 4 * G + sub;
+        if (ch == 0 && t < n) part[t * kPart + kMix] = s;
+    }
+    // accumulator layout: lane holds rows 4*g .. 4*g+3 (tokens), column r (mix)
+    const int64_t t0 = tbase + 4 * g;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        const int mix = nt * 16 + r;
+        if (mix < kMix) {
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+                if (t0 + ii < n) part[(t0 + ii) * kPart + mix] = acc[nt][ii];
         }
     }
 }
 
 // ------------------------------------------------------------------ finalize
+// 16 lanes per token (a 64-lane wave holds 4 tokens). Lane e owns partial
+// entries e and 16 + e (dots 0..23, sum of squares at 24) and, in the split,
+// comb entry C[e/4][e%4]; lanes 0..3 also own pre[e], lanes 4..7 post[e-4]. Row
+// sums combine lanes e^1, e^2 (same row), column sums lanes e^4, e^8 (same column).
+constexpr int kFinBlock = 256;
+
+// DPP lane exchanges inside a row of 16 lanes (no LDS round trip):
+// quad_perm [1,0,3,2] / [2,3,0,1] swap neighbours / pairs, row_ror:n rotates by n.
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
+}
+constexpr int kQuadSwap1 = 0xb1, kQuadSwap2 = 0x4e, kRowRor4 = 0x124, kRowRor8 = 0x128;
+
+__device__ __forceinline__ float row_sum16(float v) {   // lanes 4r..4r+3
+    v += dpp<kQuadSwap1>(v);
+    return v + dpp<kQuadSwap2>(v);
+}
+__device__ __forceinline__ float col_sum16(float v) {   // lanes k, k+4, k+8, k+12
+    v += dpp<kRowRor8>(v);
+    return v + dpp<kRowRor4>(v);
+}
+
 template <bool kSplit>
-__global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ part, int nsplit,
-                                                       int64_t n, int64_t D, float norm_eps,
-                                                       const float* __restrict__ scale,
-                                                       const float* __restrict__ base, int iters,
-                                                       float eps, float* __restrict__ mixes,
-                                                       float* __restrict__ pre, float* __restrict__ post,
-                                                       float* __restrict__ comb) {
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (t >= n) return;
-    float acc[kMix + 1];
-#pragma unroll
-    for (int i = 0; i <= kMix; ++i) acc[i] = 0.f;
+__global__ __launch_bounds__(kFinBlock) void finalize_kernel(const float* __restrict__ part, int nsplit,
+                                                             int64_t n, int64_t D, float norm_eps,
+                                                             const float* __restrict__ scale,
+                                                             const float* __restrict__ base, int iters,
+                                                             float eps, float* __restrict__ mixes,
+                                                             float* __restrict__ pre, float* __restrict__ post,
+                                                             float* __restrict__ comb) {
+    const int e = threadIdx.x & 15;
+    const int64_t t = ((int64_t)blockIdx.x * kFinBlock + threadIdx.x) >> 4;
+    const bool ok = t < n;                 // whole 16-lane groups share t
+    const int64_t tt = ok ? t : 0;
+    // fixed-order reduction over the channel slices
+    float a0 = 0.f, a1 = 0.f;
     for (int s = 0; s < nsplit; ++s) {
-        const float* p = part + ((int64_t)s * n + t) * kPart;
-        const float4* p4 = reinterpret_cast<const float4*>(p);
-#pragma unroll
-        for (int q = 0; q < kMix / 4; ++q) {
-            const float4 v = p4[q];
-            acc[4 * q] += v.x; acc[4 * q + 1] += v.y; acc[4 * q + 2] += v.z; acc[4 * q + 3] += v.w;
-        }
-        acc[kMix] += p[kMix];
+        const float* p = part + ((int64_t)s * n + tt) * kPart;
+        a0 += p[e];
+        a1 += p[16 + e];                   // entries 16..31; 25..31 are never read below
     }
-    const float rstd = 1.0f / sqrtf(acc[kMix] / (float)D + norm_eps);
-    float m[kMix];
-#pragma unroll
-    for (int i = 0; i < kMix; ++i) m[i] = acc[i] * rstd;
-    if (mixes) {
-        float4* dst = reinterpret_cast<float4*>(mixes + t * kMix);
-#pragma unroll
-        for (int q = 0; q < kMix / 4; ++q) dst[q] = make_float4(m[4 * q], m[4 * q + 1], m[4 * q + 2], m[4 * q + 3]);
+    const float sumsq = __shfl(a1, (threadIdx.x & ~15) + (kMix - 16));
+    const float rstd = 1.0f / sqrtf(sumsq / (float)D + norm_eps);
+    const float m0 = a0 * rstd;            // mixes[e]
+    const float m1 = a1 * rstd;            // mixes[16 + e] (valid for e < 8)
+    if (mixes && ok) {
+        mixes[t * kMix + e] = m0;
+        if (e < kMix - 16) mixes[t * kMix + 16 + e] = m1;
     }
     if constexpr (kSplit) {
-        float p[kHC], q[kHC], C[kHC * kHC];
-        split_sinkhorn(m, scale, base, iters, eps, p, q, C);
-        store_coeffs(t, p, q, C, pre, post, comb);
+        // comb logit of entry e is mixes[8 + e]: lane 8+e's m0 for e < 8, lane e-8's m1 otherwise
+        const int lane16 = threadIdx.x & ~15;
+        const float lo = __shfl(m0, lane16 + ((8 + e) & 15));
+        const float hi = __shfl(m1, lane16 + ((e + 8) & 15));
+        const float m = e < 8 ? lo : hi;
+        float c = m * scale[2] + base[8 + e];
+        // row softmax (max subtracted), + eps
+        float mx = fmaxf(c, dpp<kQuadSwap1>(c));
+        mx = fmaxf(mx, dpp<kQuadSwap2>(mx));
+        c = __expf(c - mx);
+        c = c * __builtin_amdgcn_rcpf(row_sum16(c)) + eps;
+        c *= __builtin_amdgcn_rcpf(col_sum16(c) + eps);
+        for (int it = 1; it < iters; ++it) {
+            c *= __builtin_amdgcn_rcpf(row_sum16(c) + eps);
+            c *= __builtin_amdgcn_rcpf(col_sum16(c) + eps);
+        }
+        if (ok) {
+            comb[t * 16 + e] = c;
+            if (e < kHC) pre[t * kHC + e] = sigmoid(m0 * scale[0] + base[e]) + eps;
+            else if (e < 2 * kHC) post[t * kHC + e - kHC] = 2.0f * sigmoid(m0 * scale[1] + base[e]);
+        }
     }
 }
 
@@ -565,12 +1013,14 @@ PassPlan plan_pass(int64_t n, int64_t d) {
     PassPlan p{};
     p.tiles = ceil_div(n, kTokWG);
     p.nchunks = (int)ceil_div(d, kChunk);
-    const int64_t target_groups = 512;
+    // channel slices are whole 128-channel super-steps (the bf16 sweep's unit)
+    const int nsuper = (int)ceil_div(d, kSuper);
+    const int64_t target_groups = HC_TARGET_GROUPS;
     int64_t ns = ceil_div(target_groups, p.tiles > 0 ? p.tiles : 1);
     if (ns < 1) ns = 1;
-    if (ns > p.nchunks) ns = p.nchunks;
+    if (ns > nsuper) ns = nsuper;
     if (ns > 64) ns = 64;
-    p.chunks_per_split = (int)ceil_div(p.nchunks, ns);
+    p.chunks_per_split = (int)ceil_div(nsuper, ns) * kKbPerSuper;
     p.nsplit = (int)ceil_div(p.nchunks, p.chunks_per_split);
     p.workspace_bytes = (size_t)p.nsplit * (size_t)n * kPart * sizeof(float);
     return p;
@@ -604,18 +1054,21 @@ hipError_t launch_post(const void* f, const void* res, bool bf16, const float* p
 }
 
 namespace {
-template <bool kBf16, bool kPost, bool kPre, bool kMfma>
+template <bool kBf16, bool kPost, bool kPre>
 void launch_pass_t(const PassArgs& a, const PassPlan& p, hipStream_t stream) {
-    hipLaunchKernelGGL((pass_kernel<kBf16, kPost, kPre, kMfma>), dim3((unsigned)p.tiles, (unsigned)p.nsplit),
-                       dim3(kPassBlock), 0, stream, a);
+    const dim3 grid((unsigned)(p.tiles * p.nsplit));
+    if constexpr (kBf16)
+        hipLaunchKernelGGL((sweep_bf16_kernel<kPost, kPre>), grid, dim3(kPassBlock), 0, stream, a);
+    else
+        hipLaunchKernelGGL((pass_kernel<false, kPost, kPre>), grid, dim3(kPassBlock), 0, stream, a);
 }
 
-template <bool kBf16, bool kMfma>
+template <bool kBf16>
 void launch_pass_flags(const PassArgs& a, const PassPlan& p, bool post, bool pre, hipStream_t stream) {
-    if (post && pre) launch_pass_t<kBf16, true, true, kMfma>(a, p, stream);
-    else if (post) launch_pass_t<kBf16, true, false, kMfma>(a, p, stream);
-    else if (pre) launch_pass_t<kBf16, false, true, kMfma>(a, p, stream);
-    else launch_pass_t<kBf16, false, false, kMfma>(a, p, stream);
+    if (post && pre) launch_pass_t<kBf16, true, true>(a, p, stream);
+    else if (post) launch_pass_t<kBf16, true, false>(a, p, stream);
+    else if (pre) launch_pass_t<kBf16, false, true>(a, p, stream);
+    else launch_pass_t<kBf16, false, false>(a, p, stream);
 }
 }  // namespace
 
@@ -635,19 +1088,19 @@ hipError_t launch_pass_and_finalize(const PassRequest& r, hipStream_t stream) {
     a.d = r.d;
     a.nchunks = p.nchunks;
     a.chunks_per_split = p.chunks_per_split;
+    a.nsplit = p.nsplit;
     const bool post = r.f_prev != nullptr, pre = r.y != nullptr;
-    // Projection engine: VALU for every stream dtype.
-    if (r.bf16) launch_pass_flags<true, false>(a, p, post, pre, stream);
-    else launch_pass_flags<false, false>(a, p, post, pre, stream);
+    if (r.bf16) launch_pass_flags<true>(a, p, post, pre, stream);
+    else launch_pass_flags<false>(a, p, post, pre, stream);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const dim3 fgrid((unsigned)ceil_div(r.n, 256));
+    const dim3 fgrid((unsigned)ceil_div(r.n * 16, kFinBlock));
     if (r.split)
-        hipLaunchKernelGGL(finalize_kernel<true>, fgrid, dim3(256), 0, stream, a.part, p.nsplit, r.n,
+        hipLaunchKernelGGL(finalize_kernel<true>, fgrid, dim3(kFinBlock), 0, stream, a.part, p.nsplit, r.n,
                            r.d * kHC, r.norm_eps, r.scale, r.base, r.iters, r.eps, r.mixes, r.pre, r.post,
                            r.comb);
     else
-        hipLaunchKernelGGL(finalize_kernel<false>, fgrid, dim3(256), 0, stream, a.part, p.nsplit, r.n,
+        hipLaunchKernelGGL(finalize_kernel<false>, fgrid, dim3(kFinBlock), 0, stream, a.part, p.nsplit, r.n,
                            r.d * kHC, r.norm_eps, r.scale, r.base, r.iters, r.eps, r.mixes, r.pre, r.post,
                            r.comb);
     return hipGetLastError();
