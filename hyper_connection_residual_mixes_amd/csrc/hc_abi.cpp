@@ -32,7 +32,8 @@ size_t elem_size(int dtype) { return dtype == HC_BF16 ? 2 : 4; }
 
 // Shape rules shared by the stream entry points. Returns HC_OK or an error.
 int check_shape(int64_t n, int hc, int64_t d, int dtype) {
-    if (n < 0 || d < 1) return HC_ERR_SHAPE;
+    // d <= 2^20 keeps every per-wave byte offset of the kernels within 31 bits
+    if (n < 0 || d < 1 || d > (int64_t(1) << 20)) return HC_ERR_SHAPE;
     if (dtype != HC_F32 && dtype != HC_BF16) return HC_ERR_UNSUPPORTED;
     if (hc != kHC || d % 8 != 0) return HC_ERR_UNSUPPORTED;
     // every byte offset must fit comfortably in 63 bits

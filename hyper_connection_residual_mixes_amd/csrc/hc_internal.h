@@ -16,7 +16,9 @@ struct PassPlan {
     int nchunks;
     int chunks_per_split;
     int nsplit;
-    size_t workspace_bytes;
+    size_t partial_bytes;    // per-slice partial rows
+    size_t packed_bytes;     // weights split into bf16 terms (bf16 streams)
+    size_t workspace_bytes;  // partial_bytes + packed_bytes
 };
 PassPlan plan_pass(int64_t n, int64_t d);
 

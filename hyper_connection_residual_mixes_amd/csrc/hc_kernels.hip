@@ -676,57 +676,212 @@ __global__ __launch_bounds__(kPassBlock) void pass_kernel(PassArgs a) {
     }
 }
 
-// ------------------------------------------------------- bf16 sweep (rowwise)
-// The MFMA operand layout puts 16 tokens x 64 B in one load instruction, which
-// leaves every cache line half used per request; measured on MI355X such loads
-// stream at <= 3.9 TB/s while 256-byte row runs reach ~5.8 TB/s. So the bf16
-// sweep loads rowwise and transposes through LDS:
-//   - super-step = 128 channels. Lane (sub = lane/16, ch = lane%16) of wave w
-//     loads, for token group G (4 per wave) and stream j, 16 B at token
-//     tbase + 4G + sub, channels cs + 8ch: one instruction = 4 tokens x 256 B.
-//   - expand / collapse / sum of squares run in that layout (stores are 256 B
-//     runs too); the rounded values are then written, one 32-channel k-block at
-//     a time, into the wave's own LDS tile in MFMA A layout (row = token 4G+sub,
-//     k-group = ch%4), XOR-swizzled so both the writes and the reads are free of
-//     bank conflicts, and read back as A operands.
-//   - weights: the same LDS stage per k-block as the generic sweep (three bf16
-//     terms in B layout, double-buffered, one barrier per k-block).
+// ------------------------------------------------------------------ finalize
+// 16 lanes per token (a 64-lane wave holds 4 tokens). Lane e owns partial
+// entries e and 16 + e (dots 0..23, sum of squares at 24) and, in the split,
+// comb entry C[e/4][e%4]; lanes 0..3 also own pre[e], lanes 4..7 post[e-4]. Row
+// sums combine lanes of a quad, column sums lanes 4 apart (DPP, no LDS).
+
+// DPP lane exchanges inside a row of 16 lanes:
+// quad_perm [1,0,3,2] / [2,3,0,1] swap neighbours / pairs, row_ror:n rotates by n.
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
+}
+constexpr int kQuadSwap1 = 0xb1, kQuadSwap2 = 0x4e, kRowRor4 = 0x124, kRowRor8 = 0x128;
+
+__device__ __forceinline__ float row_sum16(float v) {   // lanes 4r..4r+3
+    v += dpp<kQuadSwap1>(v);
+    return v + dpp<kQuadSwap2>(v);
+}
+__device__ __forceinline__ float col_sum16(float v) {   // lanes k, k+4, k+8, k+12
+    v += dpp<kRowRor8>(v);
+    return v + dpp<kRowRor4>(v);
+}
+
+struct FinalizeArgs {
+    const float* part;     // [nsplit][n][kPart]
+    int nsplit;
+    int64_t n;
+    int64_t D;             // hc * d
+    float norm_eps;
+    const float* scale;    // split only
+    const float* base;
+    int iters;
+    float eps;
+    bool split;
+    float* mixes;          // nullable
+    float* pre;
+    float* post;
+    float* comb;
+};
+
+// Token t (shared by the 16-lane group; t >= n: computes on token 0, stores
+// nothing), lane e of the group. Every lane of the wave must call it.
+__device__ __forceinline__ void finalize16(const FinalizeArgs& f, int64_t t, int e) {
+    const bool ok = t < f.n;
+    const int64_t tt = ok ? t : 0;
+    // fixed-order reduction over the channel slices
+    float a0 = 0.f, a1 = 0.f;
+    for (int s = 0; s < f.nsplit; ++s) {
+        const float* p = f.part + ((int64_t)s * f.n + tt) * kPart;
+        a0 += p[e];
+        a1 += p[16 + e];                   // entries 16..31; 25..31 are never used below
+    }
+    const int lane16 = (threadIdx.x & 63) & ~15;
+    const float sumsq = __shfl(a1, lane16 + (kMix - 16));
+    const float rstd = 1.0f / sqrtf(sumsq / (float)f.D + f.norm_eps);
+    const float m0 = a0 * rstd;            // mixes[e]
+    const float m1 = a1 * rstd;            // mixes[16 + e] (valid for e < 8)
+    if (f.mixes && ok) {
+        f.mixes[t * kMix + e] = m0;
+        if (e < kMix - 16) f.mixes[t * kMix + 16 + e] = m1;
+    }
+    if (!f.split) return;                  // uniform
+    // comb logit of entry e is mixes[8 + e]: lane 8+e's m0 for e < 8, lane e-8's m1 otherwise
+    const float lo = __shfl(m0, lane16 + ((8 + e) & 15));
+    const float hi = __shfl(m1, lane16 + ((e + 8) & 15));
+    const float m = e < 8 ? lo : hi;
+    float c = m * f.scale[2] + f.base[8 + e];
+    // row softmax (max subtracted), + eps
+    float mx = fmaxf(c, dpp<kQuadSwap1>(c));
+    mx = fmaxf(mx, dpp<kQuadSwap2>(mx));
+    c = __expf(c - mx);
+    c = c * __builtin_amdgcn_rcpf(row_sum16(c)) + f.eps;
+    c *= __builtin_amdgcn_rcpf(col_sum16(c) + f.eps);
+    for (int it = 1; it < f.iters; ++it) {
+        c *= __builtin_amdgcn_rcpf(row_sum16(c) + f.eps);
+        c *= __builtin_amdgcn_rcpf(col_sum16(c) + f.eps);
+    }
+    if (ok) {
+        f.comb[t * 16 + e] = c;
+        if (e < kHC) f.pre[t * kHC + e] = sigmoid(m0 * f.scale[0] + f.base[e]) + f.eps;
+        else if (e < 2 * kHC) f.post[t * kHC + e - kHC] = 2.0f * sigmoid(m0 * f.scale[1] + f.base[e]);
+    }
+}
+
+constexpr int kFinBlock = 256;
+
+__global__ __launch_bounds__(kFinBlock) void finalize_kernel(FinalizeArgs f) {
+    finalize16(f, ((int64_t)blockIdx.x * kFinBlock + threadIdx.x) >> 4, threadIdx.x & 15);
+}
+
+// ------------------------------------------------- bf16 sweep (stream-stationary)
+// Loading in the MFMA operand layout (16 token rows x 64 B per instruction) caps
+// reads at ~3.9 TB/s on MI355X, while 256-byte row runs reach ~5.8 TB/s, so
+// streams are loaded rowwise and transposed through LDS:
+//   - workgroup = 4 waves x 16 tokens; super-step = 128 channels. Lane
+//     (sub = lane/16, ch = lane%16) of wave w loads, for token group G (4 per
+//     wave) and stream j, 16 B at token 16w + 4G + sub, channels cs + 8ch: one
+//     instruction = 4 tokens x 256 B. Expand / collapse / sum of squares run in
+//     that layout (stores are 256 B runs too).
+//   - every wave writes its rounded values, all 4 streams, into the shared LDS
+//     A region in MFMA A layout (row = token, k-group = 8 channels),
+//     XOR-swizzled so that writes and reads are free of bank conflicts.
+//   - in the MFMA phase wave w owns stream j = w for all 64 tokens (4 row tiles).
+//     Its B operands come from L2, one 16-byte load per lane each, from weights
+//     split once per call (pack_weights_kernel) into three bf16 terms (hi + mid
+//     + lo, ~24 significant bits). The 24 mix columns take 5 MFMAs per tile and
+//     k-block (no zero padding): column tile 0 = mixes 0..15 (hi, mid, lo into
+//     one accumulator); column tile 1 = [hi | mid] of mixes 16..23, then [lo | 0]
+//     of mixes 16..23 into the same accumulator, whose two 8-column halves are
+//     added once at the end. A sixth MFMA multiplies the A tile by itself: since
+//     the A and B lane layouts coincide, mfma(A, A) accumulates the tile's Gram
+//     matrix, whose diagonal is each token's sum of squares. The 4 waves'
+//     partial results (one stream each) are summed through LDS.
+//   - two barriers per super-step; the next super-step's stream loads are issued
+//     before the MFMA phase, so they overlap it.
 constexpr int kSuper = 128;              // channels per super-step
 constexpr int kKbPerSuper = kSuper / kChunk;
 constexpr int kCoefF4 = 6;               // float4 per token: post_prev, comb_prev x4, pre_mix
+constexpr int kFragsPerKb = 5;           // B operands per (stream, k-block): hi0 mid0 lo0 [hi1|mid1] [lo1|0]
 
-struct SweepLds {
-    uint4 b[2][kBf16Stage];              // weight stage, 2 x 24 KB
-    uint4 a[kWaves][kHC * 64];           // per-wave A tile of one k-block, 4 x 4 KB
-    float4 coef[kTokWG][kCoefF4];        // per-token coefficients, 6 KB
+struct Sweep2Lds {
+    uint4 a[kHC * kKbPerSuper * 4 * 64];   // [stream][k-block][row tile][lane], 64 KB
+    float4 coef[kTokWG][kCoefF4];         // 6 KB
 };
 
-__device__ __forceinline__ int a_slot(int slot) { return slot ^ ((slot >> 4) & 7); }
+// Swizzled A slot: slot = ((j*4 + kb)*4 + tile)*64 + g*16 + r. The low 3 bits are
+// XORed with (g + 4*(kb & 1)): a transposing write (lanes with the same token
+// group and stream spread over 2 k-blocks x 4 k-groups) and a lane-ordered read
+// both touch 8 distinct bank groups per 8 lanes.
+__device__ __forceinline__ int a2_slot(int j, int kb, int tile, int lane) {
+    const int slot = ((j * kKbPerSuper + kb) * 4 + tile) * 64 + lane;
+    return slot ^ (((lane >> 4) + 4 * (kb & 1)) & 7);
+}
+
+// Splits 8 fp32 weights into three bf16 terms (w ~ hi + mid + lo).
+__device__ __forceinline__ void split3(const float4& a, const float4& b, uint4& hi, uint4& mid, uint4& lo) {
+    const float w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t h[4], m[4], l[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float x0 = w[2 * q], x1 = w[2 * q + 1];
+        h[q] = pack_bf16x2(x0, x1);
+        const float r0 = x0 - bf16_lo(h[q]), r1 = x1 - bf16_hi(h[q]);
+        m[q] = pack_bf16x2(r0, r1);
+        l[q] = pack_bf16x2(r0 - bf16_lo(m[q]), r1 - bf16_hi(m[q]));
+    }
+    hi = make_uint4(h[0], h[1], h[2], h[3]);
+    mid = make_uint4(m[0], m[1], m[2], m[3]);
+    lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+// Packed weights: for stream j and 32-channel k-block kbg, 5 B operands of 64
+// lanes x 16 B in v_mfma_f32_16x16x32_bf16 layout (lane: k-group g = lane/16,
+// column col = lane%16, channels kbg*32 + 8g .. +8 of stream j):
+//   0, 1, 2: hi, mid, lo of row col (mixes 0..15)
+//   3: hi of row 16 + col (col < 8), mid of row 16 + col - 8 (col >= 8)
+//   4: lo of row 16 + col (col < 8), zero (col >= 8)
+// Channels >= d are zero. One thread per (j, kbg, lane).
+__global__ __launch_bounds__(256) void pack_weights_kernel(const float* __restrict__ W, int64_t d, int nkb,
+                                                           uint4* __restrict__ packed) {
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= (int64_t)kHC * nkb * 64) return;
+    const int lane = (int)(gid & 63);
+    const int64_t jk = gid >> 6;                                    // j * nkb + kbg
+    const int j = (int)(jk / nkb), kbg = (int)(jk - (int64_t)j * nkb);
+    const int g = lane >> 4, col = lane & 15;
+    const int64_t e0 = (int64_t)kbg * kChunk + g * 8;
+    float4 w0a = make_float4(0.f, 0.f, 0.f, 0.f), w0b = w0a, w1a = w0a, w1b = w0a;
+    if (e0 < d) {                                                   // d % 8 == 0: whole groups
+        const float4* r0 = reinterpret_cast<const float4*>(W + (int64_t)col * kHC * d + (int64_t)j * d + e0);
+        const float4* r1 =
+            reinterpret_cast<const float4*>(W + (int64_t)(16 + (col & 7)) * kHC * d + (int64_t)j * d + e0);
+        w0a = r0[0];
+        w0b = r0[1];
+        w1a = r1[0];
+        w1b = r1[1];
+    }
+    uint4 h0, m0, l0, h1, m1, l1;
+    split3(w0a, w0b, h0, m0, l0);
+    split3(w1a, w1b, h1, m1, l1);
+    uint4* dst = packed + jk * kFragsPerKb * 64 + lane;
+    dst[0 * 64] = h0;
+    dst[1 * 64] = m0;
+    dst[2 * 64] = l0;
+    const bool lo_half = col < 8;
+    dst[3 * 64] = make_uint4(lo_half ? h1.x : m1.x, lo_half ? h1.y : m1.y, lo_half ? h1.z : m1.z,
+                             lo_half ? h1.w : m1.w);
+    dst[4 * 64] = make_uint4(lo_half ? l1.x : 0u, lo_half ? l1.y : 0u, lo_half ? l1.z : 0u, lo_half ? l1.w : 0u);
+}
 
 template <bool kPost, bool kPre>
-__global__ __launch_bounds__(kPassBlock) void sweep_bf16_kernel(PassArgs a) {
-    static_assert(kTokWave == 16, "the rowwise sweep uses one 16-token tile per wave");
-    __shared__ SweepLds lds;
+__global__ __launch_bounds__(kPassBlock, 2) void sweep2_kernel(PassArgs a, const uint4* __restrict__ packed) {
+    static_assert(kTokWave == 16 && kWaves == kHC, "one 16-token tile and one stream per wave");
+    __shared__ Sweep2Lds lds;
 
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // scalar: uniform bases
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int sub = lane >> 4, ch = lane & 15;   // rowwise role
-    const int r = lane & 15, g = lane >> 4;      // MFMA role
     const int64_t n = a.n, d = a.d;
+    const int nkb = a.nchunks;
     const int split = (int)(blockIdx.x % (unsigned)a.nsplit);
     const int64_t group = blockIdx.x / (unsigned)a.nsplit;
-    const int64_t tbase = group * kTokWG + wave * kTokWave;
-    // this workgroup's 32-channel k-blocks [kb_begin, kb_end), whole super-steps
-    const int nkb = a.nchunks;
+    const int64_t tbase = group * kTokWG + wave * kTokWave;   // this wave's rowwise tokens
     const int kb_begin = split * a.chunks_per_split;
     const int kb_end = min(nkb, kb_begin + a.chunks_per_split);
 
-    // zero B columns 24..31; per-token coefficients of the workgroup into LDS
-    for (int z = threadIdx.x; z < 2 * 3 * kHC * 4 * 8; z += kPassBlock) {
-        const int col = 8 + (z & 7), gg = (z >> 3) & 3, j = (z >> 5) & 3, term = (z >> 7) % 3,
-                  buf = z / (3 * kHC * 4 * 8);
-        lds.b[buf][b_slot(term, 1, j, gg * 16 + col)] = make_uint4(0, 0, 0, 0);
-    }
     for (int z = threadIdx.x; z < kTokWG * kCoefF4; z += kPassBlock) {
         const int tl = z / kCoefF4, q = z - tl * kCoefF4;
         const int64_t tt = group * kTokWG + tl;
@@ -739,9 +894,6 @@ __global__ __launch_bounds__(kPassBlock) void sweep_bf16_kernel(PassArgs a) {
         lds.coef[tl][q] = v;
     }
 
-    floatx4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    float sumsq[4] = {0.f, 0.f, 0.f, 0.f};
-
     // buffer resources based at the wave's first token; ranges end at token n
     const int64_t row_x = kHC * d * 2, row_f = d * 2;   // bytes per token
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(static_cast<const char*>(a.res) + tbase * row_x, (n - tbase) * row_x);
@@ -751,61 +903,53 @@ __global__ __launch_bounds__(kPassBlock) void sweep_bf16_kernel(PassArgs a) {
                                                 kPost ? (n - tbase) * row_x : 0);
     const __amdgpu_buffer_rsrc_t ry = make_rsrc(kPre ? static_cast<char*>(a.y) + tbase * row_f : nullptr,
                                                 kPre ? (n - tbase) * row_f : 0);
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.hc_fn, (int64_t)kMix * kHC * d * 4);
-    // per-lane offsets (token sub of each group, channel 8*ch); groups, streams and
-    // the super-step go into the scalar offset
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(packed, (int64_t)kHC * nkb * kFragsPerKb * 64 * 16);
     const uint32_t lane_x = (uint32_t)(sub * row_x + ch * 16);
     const uint32_t lane_f = (uint32_t)(sub * row_f + ch * 16);
-    // weight fetch offsets of this thread: hc_fn[i][j*d + 4*c4] for idx = tid + q*256
-    uint32_t lane_w[kStageLoads];
-    int c4w[kStageLoads];
+    const uint32_t lane_p = (uint32_t)(lane * 16);
+    const int g = lane >> 4, col = lane & 15;   // MFMA role: k-group, column
+
+    floatx4_t acc[4][2], gram[4];
 #pragma unroll
-    for (int q = 0; q < kStageLoads; ++q) {
-        const int idx = threadIdx.x + q * kPassBlock;
-        const int i = idx >> 5, j = (idx >> 3) & 3;
-        c4w[q] = idx & 7;
-        lane_w[q] = (uint32_t)(((int64_t)i * kHC * d + (int64_t)j * d + c4w[q] * 4) * 4);
-    }
-    auto fetch_w = [&](float4 (&w)[kStageLoads], int ci) {
+    for (int q = 0; q < 4; ++q) acc[q][0] = acc[q][1] = gram[q] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+    Raw8<true> X[4][kHC], F[4];
+    auto load_x = [&](int kb0) {
+        const int64_t cs = (int64_t)kb0 * kChunk, c = cs + ch * 8;
+        const bool c_ok = c < d && c < (int64_t)kb_end * kChunk;
 #pragma unroll
-        for (int q = 0; q < kStageLoads; ++q) {
-            const bool ok = (int64_t)ci * kChunk + c4w[q] * 4 < d;
-            w[q] = buf_load16f(rw, ok ? lane_w[q] : kOffMasked, (uint32_t)(ci * kChunk * 4));
+        for (int G = 0; G < 4; ++G) {
+            const bool live = c_ok && tbase + 4 * G + sub < n;   // masked lanes read zeros
+            const uint32_t vx = live ? lane_x : kOffMasked, vf = live ? lane_f : kOffMasked;
+#pragma unroll
+            for (int j = 0; j < kHC; ++j)
+                X[G][j].w = buf_load16(rx, vx, (uint32_t)((4 * G * kHC + j) * row_f + cs * 2));
+            if constexpr (kPost) F[G].w = buf_load16(rf, vf, (uint32_t)(4 * G * row_f + cs * 2));
         }
     };
+    // B operands of the next k-block to multiply (one k-block ahead, carried
+    // across super-steps so the elementwise phase hides their latency)
+    uint4 Bf[kFragsPerKb];
+    auto load_b = [&](int kbg) {
+        if (kbg < kb_end) {
+#pragma unroll
+            for (int q = 0; q < kFragsPerKb; ++q)
+                Bf[q] = buf_load16(rp, lane_p, (uint32_t)((((int64_t)wave * nkb + kbg) * kFragsPerKb + q) * 64 * 16));
+        }
+    };
+    if (kb_begin < kb_end) load_x(kb_begin);
+    load_b(kb_begin);
+    __syncthreads();   // coefficients
 
-    if (kb_begin < kb_end) {
-        float4 w0[kStageLoads];
-        fetch_w(w0, kb_begin);
-        commit_weights<true>(lds.b[0], w0);
-    }
-    __syncthreads();
-
-    int buf = 0;
     for (int kb0 = kb_begin; kb0 < kb_end; kb0 += kKbPerSuper) {
-        const int64_t cs = (int64_t)kb0 * kChunk;     // first channel of the super-step
-        const int64_t c = cs + ch * 8;
+        const int64_t cs = (int64_t)kb0 * kChunk, c = cs + ch * 8;
         const bool c_ok = c < d && c < (int64_t)kb_end * kChunk;
-        // lanes past token n or channel d are masked
-        uint32_t vx[4], vf[4];
+        // expand / collapse / sum of squares, rowwise, two channels (one packed
+        // word per stream) at a time; results into the A region
 #pragma unroll
         for (int G = 0; G < 4; ++G) {
             const bool live = c_ok && tbase + 4 * G + sub < n;
-            vx[G] = live ? lane_x : kOffMasked;
-            vf[G] = live ? lane_f : kOffMasked;
-        }
-        Raw8<true> X[4][kHC], F[4];
-#pragma unroll
-        for (int G = 0; G < 4; ++G) {
-#pragma unroll
-            for (int j = 0; j < kHC; ++j)
-                X[G][j].w = buf_load16(rx, vx[G], (uint32_t)((4 * G * kHC + j) * row_f + cs * 2));
-            if constexpr (kPost) F[G].w = buf_load16(rf, vf[G], (uint32_t)(4 * G * row_f + cs * 2));
-        }
-        // expand / collapse / sum of squares, rowwise, two channels (one packed
-        // word per stream) at a time; the rounded streams go back into X
-#pragma unroll
-        for (int G = 0; G < 4; ++G) {
+            const uint32_t vx = live ? lane_x : kOffMasked, vf = live ? lane_f : kOffMasked;
             const float4* cf = lds.coef[wave * kTokWave + 4 * G + sub];
             float pk[kHC], cm[kHC * kHC], pim[kHC];
             if constexpr (kPost) {
@@ -844,162 +988,94 @@ __global__ __launch_bounds__(kPassBlock) void sweep_bf16_kernel(PassArgs a) {
 #pragma unroll
                     for (int k = 0; k < kHC; ++k) xw[k] = (&X[G][k].w.x)[w] = ow[k];
                 }
-                float y0 = 0.f, y1 = 0.f;
+                if constexpr (kPre) {
+                    float y0 = 0.f, y1 = 0.f;
 #pragma unroll
-                for (int j = 0; j < kHC; ++j) {
-                    const float v0 = bf16_lo(xw[j]), v1 = bf16_hi(xw[j]);
-                    if constexpr (kPre) {
-                        y0 = fmaf(pim[j], v0, y0);
-                        y1 = fmaf(pim[j], v1, y1);
+                    for (int j = 0; j < kHC; ++j) {
+                        y0 = fmaf(pim[j], bf16_lo(xw[j]), y0);
+                        y1 = fmaf(pim[j], bf16_hi(xw[j]), y1);
                     }
-                    sumsq[G] = fmaf(v0, v0, sumsq[G]);
-                    sumsq[G] = fmaf(v1, v1, sumsq[G]);
+                    yw[w] = pack_bf16x2(y0, y1);
                 }
-                yw[w] = pack_bf16x2(y0, y1);
             }
             if constexpr (kPost) {
 #pragma unroll
                 for (int k = 0; k < kHC; ++k)
-                    buf_store16(X[G][k].w, ro, vx[G], (uint32_t)((4 * G * kHC + k) * row_f + cs * 2));
+                    buf_store16(X[G][k].w, ro, vx, (uint32_t)((4 * G * kHC + k) * row_f + cs * 2));
             }
             if constexpr (kPre)
-                buf_store16(make_uint4(yw[0], yw[1], yw[2], yw[3]), ry, vf[G], (uint32_t)(4 * G * row_f + cs * 2));
-            // keep the sum of squares here: otherwise it is sunk past the k-block loop
-            // and the unpacked values of all groups stay live across it
-            asm volatile("" : "+v"(sumsq[G]));
-            __builtin_amdgcn_sched_barrier(0);   // one token group's temporaries at a time
+                buf_store16(make_uint4(yw[0], yw[1], yw[2], yw[3]), ry, vf, (uint32_t)(4 * G * row_f + cs * 2));
+            // A layout: tile = wave, row = 4G + sub, k-block = ch / 4, k-group = ch % 4
+#pragma unroll
+            for (int j = 0; j < kHC; ++j)
+                lds.a[a2_slot(j, ch >> 2, wave, (ch & 3) * 16 + 4 * G + sub)] = X[G][j].w;
+            __builtin_amdgcn_sched_barrier(0);
         }
-        // projection, one k-block at a time (kept rolled: bounded register lifetimes)
+        // next super-step's streams: in flight during the MFMA phase
+        if (kb0 + kKbPerSuper < kb_end) load_x(kb0 + kKbPerSuper);
+        __syncthreads();   // A region complete
+
+        // MFMA phase: stream j = wave, 4 row tiles, the super-step's k-blocks; once a
+        // k-block's MFMAs are issued its B registers take the next k-block
 #pragma unroll 1
         for (int k = 0; k < kKbPerSuper; ++k) {
-            const int ci = kb0 + k;
-            if (ci >= kb_end) break;                   // uniform across the workgroup
-            const bool more = ci + 1 < kb_end;
-            float4 wnext[kStageLoads];
-            if (more) fetch_w(wnext, ci + 1);
-            uint4* at = lds.a[wave];
-            if ((ch >> 2) == k) {
+            const int kbg = kb0 + k;
+            if (kbg >= kb_end) break;   // uniform
 #pragma unroll
-                for (int G = 0; G < 4; ++G)
+            for (int tile = 0; tile < 4; ++tile) {
+                const bf16x8_t A = __builtin_bit_cast(bf16x8_t, lds.a[a2_slot(wave, k, tile, lane)]);
 #pragma unroll
-                    for (int j = 0; j < kHC; ++j) at[a_slot(j * 64 + (ch & 3) * 16 + 4 * G + sub)] = X[G][j].w;
+                for (int q = 0; q < kFragsPerKb; ++q)
+                    acc[tile][q < 3 ? 0 : 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        A, __builtin_bit_cast(bf16x8_t, Bf[q]), acc[tile][q < 3 ? 0 : 1], 0, 0, 0);
+                gram[tile] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, A, gram[tile], 0, 0, 0);
             }
-            const uint4* B = lds.b[buf];
-#pragma unroll
-            for (int j = 0; j < kHC; ++j) {
-                const bf16x8_t A = __builtin_bit_cast(bf16x8_t, at[a_slot(j * 64 + lane)]);
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                    for (int term = 0; term < 3; ++term) {
-                        const bf16x8_t Bv = __builtin_bit_cast(bf16x8_t, B[b_slot(term, nt, j, lane)]);
-                        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bv, acc[nt], 0, 0, 0);
-                    }
-                __builtin_amdgcn_sched_barrier(0);   // one stream's 6 B fragments live at a time
-            }
-            if (more) commit_weights<true>(lds.b[buf ^ 1], wnext);
-            __syncthreads();
-            buf ^= 1;
+            load_b(kbg + 1);
         }
+        __syncthreads();   // A region consumed
     }
 
-    // partial results of this (token group, channel slice)
     float* part = a.part + (int64_t)split * n * kPart;
+    // column tile 1: mixes 16 + c = columns c ([hi | lo] part) + c + 8 ([mid] part)
 #pragma unroll
-    for (int G = 0; G < 4; ++G) {
-        float s = sumsq[G];
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 4);
-        s += __shfl_xor(s, 8);
-        const int64_t t = tbase + 4 * G + sub;
-        if (ch == 0 && t < n) part[t * kPart + kMix] = s;
-    }
-    // accumulator layout: lane holds rows 4*g .. 4*g+3 (tokens), column r (mix)
-    const int64_t t0 = tbase + 4 * g;
+    for (int tile = 0; tile < 4; ++tile)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-        const int mix = nt * 16 + r;
-        if (mix < kMix) {
+        for (int ii = 0; ii < 4; ++ii) acc[tile][1][ii] += dpp<kRowRor8>(acc[tile][1][ii]);
+    // partial projections and sums of squares (Gram diagonal: row 4g + ii sits in
+    // column 4g + ii) of the 4 streams: sum over waves through LDS
+    float* red = reinterpret_cast<float*>(lds.a);   // [wave][tile][nt][ii][lane], 32 KB
+    float* red_ss = red + kWaves * 2048;            // [wave][tile][row], 1 KB
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii)
-                if (t0 + ii < n) part[(t0 + ii) * kPart + mix] = acc[nt][ii];
+    for (int tile = 0; tile < 4; ++tile)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) red[(((wave * 4 + tile) * 2 + nt) * 4 + ii) * 64 + lane] = acc[tile][nt][ii];
+#pragma unroll
+    for (int tile = 0; tile < 4; ++tile)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+            if (col == 4 * g + ii) red_ss[(wave * 4 + tile) * 16 + col] = gram[tile][ii];
+    __syncthreads();
+    for (int e = threadIdx.x; e < 4 * 2 * 4 * 64; e += kPassBlock) {
+        const int l = e & 63, ii = (e >> 6) & 3, nt = (e >> 8) & 1, tile = e >> 9;
+        const int mix = nt * 16 + (l & 15);
+        const int64_t t = group * kTokWG + tile * 16 + 4 * (l >> 4) + ii;
+        if (mix < kMix && t < n) {
+            float s = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) s += red[w * 2048 + e];
+            part[t * kPart + mix] = s;
         }
     }
-}
-
-// ------------------------------------------------------------------ finalize
-// 16 lanes per token (a 64-lane wave holds 4 tokens). Lane e owns partial
-// entries e and 16 + e (dots 0..23, sum of squares at 24) and, in the split,
-// comb entry C[e/4][e%4]; lanes 0..3 also own pre[e], lanes 4..7 post[e-4]. Row
-// sums combine lanes e^1, e^2 (same row), column sums lanes e^4, e^8 (same column).
-constexpr int kFinBlock = 256;
-
-// DPP lane exchanges inside a row of 16 lanes (no LDS round trip):
-// quad_perm [1,0,3,2] / [2,3,0,1] swap neighbours / pairs, row_ror:n rotates by n.
-template <int kCtrl>
-__device__ __forceinline__ float dpp(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
-}
-constexpr int kQuadSwap1 = 0xb1, kQuadSwap2 = 0x4e, kRowRor4 = 0x124, kRowRor8 = 0x128;
-
-__device__ __forceinline__ float row_sum16(float v) {   // lanes 4r..4r+3
-    v += dpp<kQuadSwap1>(v);
-    return v + dpp<kQuadSwap2>(v);
-}
-__device__ __forceinline__ float col_sum16(float v) {   // lanes k, k+4, k+8, k+12
-    v += dpp<kRowRor8>(v);
-    return v + dpp<kRowRor4>(v);
-}
-
-template <bool kSplit>
-__global__ __launch_bounds__(kFinBlock) void finalize_kernel(const float* __restrict__ part, int nsplit,
-                                                             int64_t n, int64_t D, float norm_eps,
-                                                             const float* __restrict__ scale,
-                                                             const float* __restrict__ base, int iters,
-                                                             float eps, float* __restrict__ mixes,
-                                                             float* __restrict__ pre, float* __restrict__ post,
-                                                             float* __restrict__ comb) {
-    const int e = threadIdx.x & 15;
-    const int64_t t = ((int64_t)blockIdx.x * kFinBlock + threadIdx.x) >> 4;
-    const bool ok = t < n;                 // whole 16-lane groups share t
-    const int64_t tt = ok ? t : 0;
-    // fixed-order reduction over the channel slices
-    float a0 = 0.f, a1 = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-        const float* p = part + ((int64_t)s * n + tt) * kPart;
-        a0 += p[e];
-        a1 += p[16 + e];                   // entries 16..31; 25..31 are never read below
-    }
-    const float sumsq = __shfl(a1, (threadIdx.x & ~15) + (kMix - 16));
-    const float rstd = 1.0f / sqrtf(sumsq / (float)D + norm_eps);
-    const float m0 = a0 * rstd;            // mixes[e]
-    const float m1 = a1 * rstd;            // mixes[16 + e] (valid for e < 8)
-    if (mixes && ok) {
-        mixes[t * kMix + e] = m0;
-        if (e < kMix - 16) mixes[t * kMix + 16 + e] = m1;
-    }
-    if constexpr (kSplit) {
-        // comb logit of entry e is mixes[8 + e]: lane 8+e's m0 for e < 8, lane e-8's m1 otherwise
-        const int lane16 = threadIdx.x & ~15;
-        const float lo = __shfl(m0, lane16 + ((8 + e) & 15));
-        const float hi = __shfl(m1, lane16 + ((e + 8) & 15));
-        const float m = e < 8 ? lo : hi;
-        float c = m * scale[2] + base[8 + e];
-        // row softmax (max subtracted), + eps
-        float mx = fmaxf(c, dpp<kQuadSwap1>(c));
-        mx = fmaxf(mx, dpp<kQuadSwap2>(mx));
-        c = __expf(c - mx);
-        c = c * __builtin_amdgcn_rcpf(row_sum16(c)) + eps;
-        c *= __builtin_amdgcn_rcpf(col_sum16(c) + eps);
-        for (int it = 1; it < iters; ++it) {
-            c *= __builtin_amdgcn_rcpf(row_sum16(c) + eps);
-            c *= __builtin_amdgcn_rcpf(col_sum16(c) + eps);
-        }
-        if (ok) {
-            comb[t * 16 + e] = c;
-            if (e < kHC) pre[t * kHC + e] = sigmoid(m0 * scale[0] + base[e]) + eps;
-            else if (e < 2 * kHC) post[t * kHC + e - kHC] = 2.0f * sigmoid(m0 * scale[1] + base[e]);
+    if (threadIdx.x < kTokWG) {   // token tile*16 + row of the group
+        const int tile = threadIdx.x >> 4, row = threadIdx.x & 15;
+        const int64_t t = group * kTokWG + threadIdx.x;
+        if (t < n) {
+            float s = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) s += red_ss[(w * 4 + tile) * 16 + row];
+            part[t * kPart + kMix] = s;
         }
     }
 }
@@ -1022,7 +1098,10 @@ PassPlan plan_pass(int64_t n, int64_t d) {
     if (ns > 64) ns = 64;
     p.chunks_per_split = (int)ceil_div(nsuper, ns) * kKbPerSuper;
     p.nsplit = (int)ceil_div(p.nchunks, p.chunks_per_split);
-    p.workspace_bytes = (size_t)p.nsplit * (size_t)n * kPart * sizeof(float);
+    // [partial rows: nsplit x n x 32 floats][packed weights: 4 streams x nchunks x 5 x 1 KB]
+    p.partial_bytes = (size_t)p.nsplit * (size_t)n * kPart * sizeof(float);
+    p.packed_bytes = (size_t)kHC * (size_t)p.nchunks * kFragsPerKb * 64 * 16;
+    p.workspace_bytes = p.partial_bytes + p.packed_bytes;
     return p;
 }
 
@@ -1054,21 +1133,16 @@ hipError_t launch_post(const void* f, const void* res, bool bf16, const float* p
 }
 
 namespace {
-template <bool kBf16, bool kPost, bool kPre>
-void launch_pass_t(const PassArgs& a, const PassPlan& p, hipStream_t stream) {
-    const dim3 grid((unsigned)(p.tiles * p.nsplit));
-    if constexpr (kBf16)
-        hipLaunchKernelGGL((sweep_bf16_kernel<kPost, kPre>), grid, dim3(kPassBlock), 0, stream, a);
-    else
-        hipLaunchKernelGGL((pass_kernel<false, kPost, kPre>), grid, dim3(kPassBlock), 0, stream, a);
+template <bool kPost, bool kPre>
+void launch_sweep2_t(const PassArgs& a, const PassPlan& p, const uint4* packed, hipStream_t stream) {
+    hipLaunchKernelGGL((sweep2_kernel<kPost, kPre>), dim3((unsigned)(p.tiles * p.nsplit)), dim3(kPassBlock), 0,
+                       stream, a, packed);
 }
 
-template <bool kBf16>
-void launch_pass_flags(const PassArgs& a, const PassPlan& p, bool post, bool pre, hipStream_t stream) {
-    if (post && pre) launch_pass_t<kBf16, true, true>(a, p, stream);
-    else if (post) launch_pass_t<kBf16, true, false>(a, p, stream);
-    else if (pre) launch_pass_t<kBf16, false, true>(a, p, stream);
-    else launch_pass_t<kBf16, false, false>(a, p, stream);
+template <bool kPost, bool kPre>
+void launch_pass_t(const PassArgs& a, const PassPlan& p, hipStream_t stream) {
+    hipLaunchKernelGGL((pass_kernel<false, kPost, kPre>), dim3((unsigned)(p.tiles * p.nsplit)), dim3(kPassBlock), 0,
+                       stream, a);
 }
 }  // namespace
 
@@ -1089,20 +1163,40 @@ hipError_t launch_pass_and_finalize(const PassRequest& r, hipStream_t stream) {
     a.nchunks = p.nchunks;
     a.chunks_per_split = p.chunks_per_split;
     a.nsplit = p.nsplit;
+    FinalizeArgs f{};
+    f.part = a.part;
+    f.nsplit = p.nsplit;
+    f.n = r.n;
+    f.D = r.d * kHC;
+    f.norm_eps = r.norm_eps;
+    f.scale = r.scale;
+    f.base = r.base;
+    f.iters = r.iters;
+    f.eps = r.eps;
+    f.split = r.split;
+    f.mixes = r.mixes;
+    f.pre = r.pre;
+    f.post = r.post;
+    f.comb = r.comb;
     const bool post = r.f_prev != nullptr, pre = r.y != nullptr;
-    if (r.bf16) launch_pass_flags<true>(a, p, post, pre, stream);
-    else launch_pass_flags<false>(a, p, post, pre, stream);
+    if (r.bf16) {
+        // weights split into bf16 terms in MFMA B layout, once per call
+        uint4* packed = reinterpret_cast<uint4*>(static_cast<char*>(r.workspace) + p.partial_bytes);
+        hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)ceil_div((int64_t)kHC * p.nchunks * 64, 256)),
+                           dim3(256), 0, stream, r.hc_fn, r.d, p.nchunks, packed);
+        if (post && pre) launch_sweep2_t<true, true>(a, p, packed, stream);
+        else if (post) launch_sweep2_t<true, false>(a, p, packed, stream);
+        else if (pre) launch_sweep2_t<false, true>(a, p, packed, stream);
+        else launch_sweep2_t<false, false>(a, p, packed, stream);
+    } else {
+        if (post && pre) launch_pass_t<true, true>(a, p, stream);
+        else if (post) launch_pass_t<true, false>(a, p, stream);
+        else if (pre) launch_pass_t<false, true>(a, p, stream);
+        else launch_pass_t<false, false>(a, p, stream);
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const dim3 fgrid((unsigned)ceil_div(r.n * 16, kFinBlock));
-    if (r.split)
-        hipLaunchKernelGGL(finalize_kernel<true>, fgrid, dim3(kFinBlock), 0, stream, a.part, p.nsplit, r.n,
-                           r.d * kHC, r.norm_eps, r.scale, r.base, r.iters, r.eps, r.mixes, r.pre, r.post,
-                           r.comb);
-    else
-        hipLaunchKernelGGL(finalize_kernel<false>, fgrid, dim3(kFinBlock), 0, stream, a.part, p.nsplit, r.n,
-                           r.d * kHC, r.norm_eps, r.scale, r.base, r.iters, r.eps, r.mixes, r.pre, r.post,
-                           r.comb);
+    hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)ceil_div(r.n * 16, kFinBlock)), dim3(kFinBlock), 0, stream, f);
     return hipGetLastError();
 }
 

@@ -56,15 +56,18 @@ def test_version_and_status_strings():
 
 
 def test_workspace_size_rule():
-    # 64-token tiles x 32-channel steps; one 128-byte partial row per (slice, token)
+    # [one 128-byte partial row per (channel slice, token); slices are whole
+    #  128-channel steps][the weights split into bf16 terms: 4 streams x
+    #  ceil(d/32) k-blocks x 5 B operands x 1 KB]
     assert hc.workspace_size(0, 4, 5120) == 0
     assert hc.workspace_size(16, 3, 5120) == 0
     assert hc.workspace_size(16, 4, 12) == 0
     for n, d in ((16, 256), (64, 5120), (4096, 5120), (65536, 5120), (37, 264)):
         ws = hc.workspace_size(n, 4, d)
-        assert ws > 0 and ws % (128 * n) == 0
-        nsplit = ws // (128 * n)
-        assert 1 <= nsplit <= min(64, -(-d // 32))
+        part = ws - 4 * (-(-d // 32)) * 5 * 1024
+        assert part > 0 and part % (128 * n) == 0
+        nsplit = part // (128 * n)
+        assert 1 <= nsplit <= min(64, -(-d // 128))
 
 
 def _split(mixes=A, scale=B, base=C, n=16, hc_=4, iters=20, eps=1e-6, pre=A + 4096, post=A + 8192,
@@ -94,6 +97,7 @@ def test_pre_validation():
     assert _pre(n=0) == OK
     assert _pre(d=0) == SHAPE
     assert _pre(d=260) == UNSUP
+    assert _pre(d=(1 << 20) + 8) == SHAPE   # beyond the supported width
     assert _pre(dtype=2) == UNSUP
     assert _pre(hc_=2) == UNSUP
     assert _pre(x=None) == NULL
