@@ -14,13 +14,24 @@ Prints one JSON line (see the keys below). --gpus N > 1 is refused: this build r
 on one GPU.
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+
+KERNEL_SOURCES = ("hyper_connection_residual_mixes_amd/csrc/hc_kernels.hip",
+                  "hyper_connection_residual_mixes_amd/csrc/hc_internal.h")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "ffn_boundary_counters_prefill_T4096.md")
+ENTRY_KERNELS = {
+    "attn_fused": "pack_weights_kernel + sweep2_kernel<no expand, collapse> + finalize_kernel",
+    "ffn_fused": "pack_weights_kernel + sweep2_kernel<expand, collapse> + finalize_kernel",
+    "ffn_post": "post_kernel",
+}
 
 METRIC = "tokens/s and achieved HBM TB/s (% of peak), fused HC mix, d=5120, 4 streams"
 PEAK_HBM_GBS = 8000.0
@@ -37,21 +48,49 @@ def algorithmic_bytes(n: int, d: int, es: int = 2):
     return dict(attn_fused=k1, ffn_fused=k2, ffn_post=k3, block=k1 + k2 + k3)
 
 
-def cpu_baseline(inp):
-    import torch
+def kernel_source_digest() -> str:
+    """sha256 over the HIP sources; a stored counter record is valid only for the
+    kernels it was taken on."""
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
+
+def stored_traffic(entry: str):
+    """HBM bytes per launch of ``entry`` from the committed rocprofv3 counter record
+    (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for a plain copy
+    of known size), or None when the kernels changed since the counters were taken."""
+    try:
+        text = open(TRAFFIC_RECORD).read()
+    except OSError:
+        return None
+    m = re.search(r"^traffic-record: (\{.*\})$", text, flags=re.M)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return rec.get("bytes_per_launch", {}).get(entry)
+
+
+def cpu_baseline(sets_cpu):
+    """The C oracle (fp64, one thread) on the whole block for each input set."""
     import oracle
 
-    x, attn, ffn, fa, ff = inp["x"], inp["attn"], inp["ffn"], inp["f_attn"], inp["f_ffn"]
-    pi, _, _ = oracle.hc_split_sinkhorn(*inp["prev"])
-    cpu = lambda t: t.cpu() if isinstance(t, torch.Tensor) else tuple(u.cpu() for u in t)
-    x, fa, ff, pi, attn, ffn = cpu(x), cpu(fa), cpu(ff), cpu(pi), cpu(attn), cpu(ffn)
-    t0 = time.perf_counter()
-    oracle.block(x, pi, attn, ffn, fa, ff)
-    dt = time.perf_counter() - t0
-    return dict(value=x.shape[0] / dt, unit="tokens/s", cores=1, kind="oracle",
-                sample=f"the full block on one input set ({x.shape[0]} tokens, d={x.shape[-1]}), "
-                       f"single-threaded C oracle, fp64, {dt:.1f} s")
+    n_tok, dt = 0, 0.0
+    for x, prev, attn, ffn, fa, ff in sets_cpu:
+        pi, _, _ = oracle.hc_split_sinkhorn(*prev)   # collapse weights of the previous call
+        t0 = time.perf_counter()
+        oracle.block(x, pi, attn, ffn, fa, ff)
+        dt += time.perf_counter() - t0
+        n_tok += x.shape[0]
+    d = sets_cpu[0][0].shape[-1]
+    return dict(value=n_tok / dt, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"the full block (attention + FFN boundary) on {len(sets_cpu)} input sets of "
+                       f"{sets_cpu[0][0].shape[0]} tokens, d={d}: {n_tok} tokens, "
+                       f"single-threaded C oracle in fp64, {dt:.1f} s")
 
 
 def main():
@@ -61,6 +100,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--sets", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-copy-ceiling", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -87,8 +127,6 @@ def main():
                    cA=tuple(torch.empty(sh, device=dev) for sh in ((n, 4), (n, 4), (n, 4, 4))),
                    cF=tuple(torch.empty(sh, device=dev) for sh in ((n, 4), (n, 4), (n, 4, 4))))
         sets.append((inp, pi, out))
-        if s == 0:
-            first = inp
     ws = torch.empty(hc.workspace_size(n, 4, d), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -112,18 +150,15 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # whole-step timing: K steps bracketed by device synchronisation
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    # per-entry-point durations with HIP events on the launch stream (separate pass)
+    # K timed steps bracketed by device synchronisation; HIP events on the launch
+    # stream around each entry point give the per-entry-point durations of the same steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
     for i in range(args.steps):
         step(i, evs[i])
     torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
     per = {k: 1e-3 * sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
            for j, k in enumerate(("attn_fused", "ffn_fused", "ffn_post"))}
 
@@ -133,19 +168,22 @@ def main():
     eff_gbs = ab["block"] / (wall / args.steps) / 1e9
     dom = "ffn_fused"
     ach = ab[dom] / per[dom] / 1e9
-    # plain copy ceiling on the same device (1 GiB read + 1 GiB write)
-    src = torch.empty(1 << 29, dtype=torch.int16, device=dev)
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(10):
-        dst.copy_(src)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbs = 2 * src.numel() * 2 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del src, dst
+    copy_gbs = None
+    if not args.no_copy_ceiling:
+        # plain copy on the same device, 1 GiB read + 1 GiB write (also the
+        # reference dispatch for scaling the FETCH_SIZE / WRITE_SIZE counters)
+        src = torch.empty(1 << 29, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        copy_gbs = 2 * src.numel() * 2 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del src, dst
 
     result = {
         "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -158,13 +196,19 @@ def main():
         "copy_ceiling_gb_s": copy_gbs,
         "entry_point_us": {k: v * 1e6 for k, v in per.items()},
         "algorithmic_bytes": ab,
-        "roofline": {"kernel": "hc_fused_step (FFN boundary: expand + coefficients + collapse)",
+        "roofline": {"kernel": f"hc_fused_step, FFN boundary ({ENTRY_KERNELS[dom]})",
                      "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": ach / PEAK_HBM_GBS, "traffic": None},
+                     "frac": ach / PEAK_HBM_GBS, "traffic": stored_traffic(dom)},
+        "entry_point_roofline": {k: {"kernels": ENTRY_KERNELS[k], "achieved_gb_s": ab[k] / per[k] / 1e9,
+                                     "frac": ab[k] / per[k] / 1e9 / PEAK_HBM_GBS,
+                                     "traffic": stored_traffic(k)} for k in per},
     }
     if not args.no_cpu_baseline:
-        print("bench: timing the CPU oracle on one input set", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(first)
+        print("bench: timing the CPU oracle on every input set", file=sys.stderr, flush=True)
+        cpu = lambda t: t.cpu() if isinstance(t, torch.Tensor) else tuple(u.cpu() for u in t)
+        sets_cpu = [(cpu(inp["x"]), cpu(inp["prev"]), cpu(inp["attn"]), cpu(inp["ffn"]), cpu(inp["f_attn"]),
+                     cpu(inp["f_ffn"])) for inp, _, _ in sets]
+        result["cpu_baseline"] = cpu_baseline(sets_cpu)
     print(json.dumps(result), flush=True)
 
 
