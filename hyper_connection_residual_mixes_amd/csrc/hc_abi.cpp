@@ -88,7 +88,7 @@ const char* hc_status_string(int status) {
 
 size_t hc_workspace_size(int64_t n, int hc, int64_t d) {
     if (n <= 0 || check_shape(n, hc, d, HC_F32) != HC_OK) return 0;
-    return hc::plan_pass(n, d).workspace_bytes;
+    return hc::workspace_bytes(n, d);
 }
 
 int hc_split_sinkhorn(const float* mixes, const float* hc_scale, const float* hc_base, int64_t n, int hc,
@@ -147,11 +147,11 @@ int hc_mixes(const void* x, int dtype, int64_t n, int hc, int64_t d, const float
     if (n == 0) return HC_OK;
     if (!x || !hc_fn || !mixes) return HC_ERR_NULL;
     if (!aligned(x, 16) || !aligned(hc_fn, 16) || !aligned(mixes, 16)) return HC_ERR_ALIGN;
-    const hc::PassPlan plan = hc::plan_pass(n, d);
-    if (!workspace || workspace_bytes < plan.workspace_bytes) return HC_ERR_WORKSPACE;
+    const size_t ws_need = hc::workspace_bytes(n, d);
+    if (!workspace || workspace_bytes < ws_need) return HC_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return HC_ERR_ALIGN;
     const size_t es = elem_size(dtype), un = (size_t)n, ud = (size_t)d;
-    const Span outs[] = {{mixes, un * kMix * 4}, {workspace, plan.workspace_bytes}};
+    const Span outs[] = {{mixes, un * kMix * 4}, {workspace, ws_need}};
     const Span ins[] = {{x, un * kHC * ud * es}, {hc_fn, (size_t)kMix * kHC * ud * 4}};
     if (int rc = check_aliases(outs, 2, ins, 2, nullptr, 0)) return rc;
     hc::PassRequest r{};
@@ -180,8 +180,8 @@ int hc_fused_step(const void* residual, const void* f_prev, const float* post_pr
     const bool expand = f_prev != nullptr;
     if (expand && (!post_prev || !comb_prev || !streams_out)) return HC_ERR_NULL;
     if (y && !pre_mix) return HC_ERR_NULL;
-    const hc::PassPlan plan = hc::plan_pass(n, d);
-    if (!workspace || workspace_bytes < plan.workspace_bytes) return HC_ERR_WORKSPACE;
+    const size_t ws_need = hc::workspace_bytes(n, d);
+    if (!workspace || workspace_bytes < ws_need) return HC_ERR_WORKSPACE;
     const void* a16[] = {residual, hc_fn, pre, post, comb, workspace};
     for (const void* p : a16)
         if (!aligned(p, 16)) return HC_ERR_ALIGN;
@@ -199,7 +199,7 @@ int hc_fused_step(const void* residual, const void* f_prev, const float* post_pr
                          {post, un * 16},
                          {comb, un * 64},
                          {mixes, un * kMix * 4},
-                         {workspace, plan.workspace_bytes}};
+                         {workspace, ws_need}};
     const Span ins[] = {res_span,
                         {f_prev, un * ud * es},
                         {expand ? post_prev : nullptr, un * 16},

@@ -20,7 +20,9 @@ struct PassPlan {
     size_t packed_bytes;     // weights split into bf16 terms (bf16 streams)
     size_t workspace_bytes;  // partial_bytes + packed_bytes
 };
-PassPlan plan_pass(int64_t n, int64_t d);
+PassPlan plan_pass(int64_t n, int64_t d, bool bf16);
+// Workspace that covers the plans of both stream dtypes.
+size_t workspace_bytes(int64_t n, int64_t d);
 
 struct PassRequest {
     const void* res;         // streams entering the boundary [n][4][d]

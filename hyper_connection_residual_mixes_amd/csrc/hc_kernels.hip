@@ -11,15 +11,17 @@
 //   split_kernel        one lane per token: sigmoid split + Sinkhorn in registers.
 //   pre_kernel          collapse, one lane per (token, 8 channels), 128-bit loads.
 //   post_kernel         expand + combine, one lane per (token, 8 channels).
-//   pass_kernel         one sweep over a tile of 64 tokens x a channel slice:
+//   pack_weights_kernel splits hc_fn into three bf16 terms in MFMA B layout.
+//   bf16_sweep_kernel   one pass over 64 tokens x a channel slice of bf16 streams:
 //                       optional expand (previous sublayer's post/comb), optional
-//                       collapse, and the partial 24-wide projection + sum of
-//                       squares of the (rounded) streams, written to a workspace.
+//                       collapse, and the partial 24-wide projection (MFMA) and
+//                       sum of squares of the (rounded) streams, to a workspace.
+//   pass_kernel         the same pass for fp32 streams (fp32 MFMA).
 //   finalize_kernel     16 lanes per token: reduce the slice partials in a fixed
 //                       order, scale by the RMS statistic, and (optionally) split.
 //
-// All arithmetic is fp32. bf16 values are rounded to nearest-even
-// (v_cvt_pk_bf16_f32). Buffer offsets are 64-bit throughout.
+// All arithmetic is fp32 (MFMA products exact, fp32 accumulation). bf16 values
+// are rounded to nearest-even (v_cvt_pk_bf16_f32).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -36,14 +38,9 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 constexpr int kHC = 4;          // streams
 constexpr int kMix = 24;        // (2 + hc) * hc mix numbers
 constexpr int kPart = 32;       // floats per (split, token) partial row: 24 dots, sumsq, pad
-#ifndef HC_TILES
-#define HC_TILES 1
-#endif
-#ifndef HC_TARGET_GROUPS
-#define HC_TARGET_GROUPS 512
-#endif
-constexpr int kWaves = 4;           // waves per pass workgroup
-constexpr int kTiles = HC_TILES;    // 16-token MFMA row tiles per wave
+constexpr int kWaves = 4;           // waves per fp32 pass workgroup
+constexpr int kTiles = 1;           // 16-token MFMA row tiles per wave (fp32 pass)
+constexpr int kPassTargetGroups = 512;
 constexpr int kTokWave = 16 * kTiles;
 constexpr int kTokWG = kWaves * kTokWave;
 constexpr int kChunk = 32;      // channels per sweep step (4 lane groups x 8)
@@ -71,16 +68,28 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
     const int64_t b = bytes < 0 ? 0 : (bytes > 0x7ffffff0 ? 0x7ffffff0 : bytes);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)b, kRawBufferFlags);
 }
+// The scalar offset must be wave-uniform; readfirstlane states that to the
+// compiler, which otherwise may keep it in a vector register and wrap the access
+// in a loop over its distinct values.
+__device__ __forceinline__ int uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane((int)v); }
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, uniform(soff), 0);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 __device__ __forceinline__ float4 buf_load16f(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, uniform(soff), 0);
     return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
 }
+// A 16-byte store reads its data registers after issue. Nothing may overwrite
+// them in the next two cycles; the compiler does not keep that distance here
+// (a write to the first data register right after the store was seen to corrupt
+// stored values), so every such store is followed by two wait states that no
+// instruction is scheduled into.
 __device__ __forceinline__ void buf_store16(uint4 v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{v.x, v.y, v.z, v.w}, r, (int)voff, (int)soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{v.x, v.y, v.z, v.w}, r, (int)voff, uniform(soff), 0);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 1");
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // Eight consecutive elements of a row: load/store as fp32 values, plus the raw
@@ -302,23 +311,20 @@ __global__ __launch_bounds__(kEwBlock) void post_kernel(const void* __restrict__
     for (int k = 0; k < kHC; ++k) ov[k].store(out, (t * kHC + k) * d + e);
 }
 
-// ---------------------------------------------------------------- stream pass
+// ------------------------------------------------------ fp32 stream pass
 // Workgroup = 4 waves x 16 tokens. Lane (r = lane % 16, g = lane / 16) of wave w
 // owns token tile*64 + w*16 + r and, at sweep step ci, channels ci*32 + g*8 ..+8
 // of all 4 streams. The step's slice of hc_fn (24 rows x 4 streams x 32 channels)
 // is staged in LDS once per workgroup and shared by its 4 waves.
 //
-// Projection engines (A = 16 tokens x k, B = k x 16 mixes, fp32 accumulators;
-// the 24 mixes use two 16-wide column tiles whose columns 24..31 are zero):
-//   bf16 streams: v_mfma_f32_16x16x32_bf16. The bf16 stream values are exact A
-//         operands; the fp32 weights are split into three bf16 terms (hi + mid +
-//         lo, ~24 significant bits), each accumulated into the same accumulator.
-//   fp32 streams: v_mfma_f32_16x16x4f32 with the fp32 values and weights as they
-//         are; k runs over the 4 lane groups, one MFMA per (stream, channel).
+// Projection: v_mfma_f32_16x16x4f32 (A = 16 tokens x 4 channels, B = 4 channels
+// x 16 mixes, exact fp32 products, fp32 accumulators) with k running over the 4
+// lane groups, one MFMA per (stream, channel, column tile); the 24 mixes use two
+// 16-wide column tiles whose columns 24..31 are zero.
 //
-// Pipelining: while step ci is computed, the stream values of step ci+1 are
-// already loaded into registers and its weights fetched; the weights are split
-// into the other LDS buffer after step ci's MFMAs, then one barrier per step.
+// Pipelining: while step ci is computed, the weights of step ci+1 are fetched
+// from L2 and copied into the other LDS buffer after step ci's MFMAs, then one
+// barrier per step.
 //
 // Grid: one dimension, workgroup L -> (tile = L / nsplit, slice = L % nsplit).
 // Workgroups are dealt to the 8 XCDs round-robin, so with nsplit a multiple of 8
@@ -342,35 +348,13 @@ struct PassArgs {
 };
 
 constexpr int kPassBlock = kWaves * 64;
-constexpr int kBf16Stage = 3 * 2 * kHC * 64;   // uint4 per LDS buffer: term x ntile x stream x lane
 constexpr int kF32Row = kHC * kChunk + 4;      // floats per mix row of the fp32 stage (padded)
 constexpr int kF32Stage = 32 * kF32Row;        // floats per LDS buffer: 32 mix rows (24..31 zero)
 constexpr int kStageLoads = (kMix * kHC * kChunk / 4) / kPassBlock;  // float4 per thread per step
 
-// B-fragment slot (16 B) of (term, ntile, stream j, lane) in a bf16 weight stage,
-// XOR-swizzled within groups of 8 so that the split's 8-byte writes spread over
-// all banks while the MFMA's lane-ordered 16-byte reads stay conflict-free.
-// Columns 8..15 of a slot group stay in 8..15 (padding maps onto padding).
-__device__ __forceinline__ int b_slot(int term, int nt, int j, int lane) {
-    const int slot = ((term * 2 + nt) * 4 + j) * 64 + lane;
-    return slot ^ (((lane >> 4) + 4 * (j & 1)) & 7);
-}
-
-template <bool kBf16>
-struct PassLds;
-template <>
-struct PassLds<true> {
-    uint4 b[2][kBf16Stage];
-};
-template <>
-struct PassLds<false> {
+struct PassLds {
     float w[2][kF32Stage];
 };
-
-__device__ __forceinline__ uint4* lds_b(PassLds<true>& l, int buf) { return l.b[buf]; }
-__device__ __forceinline__ uint4* lds_b(PassLds<false>&, int) { return nullptr; }
-__device__ __forceinline__ float* lds_w(PassLds<false>& l, int buf) { return l.w[buf]; }
-__device__ __forceinline__ float* lds_w(PassLds<true>&, int) { return nullptr; }
 
 // Thread's share of hc_fn[i][j*d + ci*32 + 0..31] (i < 24, j < 4): kStageLoads
 // float4 values; entry q covers idx = threadIdx.x + q*256 -> i = idx/32,
@@ -391,59 +375,19 @@ __device__ __forceinline__ void fetch_weights(float4 (&w)[kStageLoads], const fl
     }
 }
 
-// Splits (bf16) or copies (fp32) the fetched weights into LDS stage buffer `dst`
-// (one buffer: kBf16Stage uint4 or kF32Stage floats).
-template <bool kBf16>
-__device__ __forceinline__ void commit_weights(void* dst, const float4 (&w)[kStageLoads]) {
+// Copies the fetched weights into LDS stage buffer `dst`, laid out as
+// [32 rows][4 streams][32 channels] with row stride kF32Row floats.
+__device__ __forceinline__ void commit_weights(float* dst, const float4 (&w)[kStageLoads]) {
 #pragma unroll
     for (int q = 0; q < kStageLoads; ++q) {
         const int idx = threadIdx.x + q * kPassBlock;
         const int i = idx >> 5, j = (idx >> 3) & 3, c4 = idx & 7;
-        if constexpr (kBf16) {
-            const float wv[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
-            uint32_t hi[2], mid[2], lo[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const float a = wv[2 * h], b = wv[2 * h + 1];
-                hi[h] = pack_bf16x2(a, b);
-                const float ra = a - bf16_lo(hi[h]), rb = b - bf16_hi(hi[h]);
-                mid[h] = pack_bf16x2(ra, rb);
-                const float sa = ra - bf16_lo(mid[h]), sb = rb - bf16_hi(mid[h]);
-                lo[h] = pack_bf16x2(sa, sb);
-            }
-            // B operand of tile nt = i/16: lane (k-group = c4/2)*16 + column i%16,
-            // 8 bf16 per lane of which this float4 fills half c4%2
-            const int nt = i >> 4, col = i & 15;
-            const int lane = (c4 >> 1) * 16 + col;
-            const int half = c4 & 1;
-            uint2* base = reinterpret_cast<uint2*>(dst);
-            base[b_slot(0, nt, j, lane) * 2 + half] = make_uint2(hi[0], hi[1]);
-            base[b_slot(1, nt, j, lane) * 2 + half] = make_uint2(mid[0], mid[1]);
-            base[b_slot(2, nt, j, lane) * 2 + half] = make_uint2(lo[0], lo[1]);
-        } else {
-            // layout [32 rows][4 streams][32 channels], row stride kF32Row floats
-            *reinterpret_cast<float4*>(static_cast<float*>(dst) + i * kF32Row + j * kChunk + c4 * 4) = w[q];
-        }
+        *reinterpret_cast<float4*>(dst + i * kF32Row + j * kChunk + c4 * 4) = w[q];
     }
 }
 
-// Raw 8-element stream data of one lane for one step (registers only).
-template <bool kBf16>
-struct Raw8;
-template <>
-struct Raw8<true> {
-    uint4 w;
-    __device__ __forceinline__ void load(const void* base, int64_t idx) {
-        w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
-    }
-    __device__ __forceinline__ void zero() { w = make_uint4(0, 0, 0, 0); }
-    __device__ __forceinline__ void to(Vec8<true>& v) const {
-        v.raw = w;
-        v.unpack();
-    }
-};
-template <>
-struct Raw8<false> {
+// Eight fp32 stream values of one lane for one step (registers only).
+struct Raw8 {
     float4 a, b;
     __device__ __forceinline__ void load(const void* base, int64_t idx) {
         const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
@@ -457,17 +401,17 @@ struct Raw8<false> {
     }
 };
 
-template <bool kBf16, bool kPost>
+template <bool kPost>
 struct StepData {
-    Raw8<kBf16> x[kHC];
-    Raw8<kBf16> f;  // used when kPost
+    Raw8 x[kHC];
+    Raw8 f;  // used when kPost
 };
 
 // Loads one step's stream values of a lane. Out-of-range lanes (token >= n or
 // channel >= d) load from token 0 / channel 0, which always exists, and get
 // zeros, so the loads are unconditional.
-template <bool kBf16, bool kPost>
-__device__ __forceinline__ void load_step(StepData<kBf16, kPost>& s, const PassArgs& a, int64_t t, bool live,
+template <bool kPost>
+__device__ __forceinline__ void load_step(StepData<kPost>& s, const PassArgs& a, int64_t t, bool live,
                                           int64_t e) {
     const int64_t tt = live ? t : 0, ee = live ? e : 0;
 #pragma unroll
@@ -511,17 +455,17 @@ __device__ __forceinline__ void load_coef(LaneCoef& co, const PassArgs& a, int64
 
 // Elementwise part of one step for one tile: expand (optional), collapse
 // (optional), sum of squares. Leaves the (rounded) stream values in xs.
-template <bool kBf16, bool kPost, bool kPre>
-__device__ __forceinline__ void step_elementwise(const PassArgs& a, const StepData<kBf16, kPost>& in,
+template <bool kPost, bool kPre>
+__device__ __forceinline__ void step_elementwise(const PassArgs& a, const StepData<kPost>& in,
                                                  const LaneCoef& co, int64_t t, bool live, int64_t e,
-                                                 Vec8<kBf16> (&xs)[kHC], float& sumsq) {
+                                                 Vec8<false> (&xs)[kHC], float& sumsq) {
     const int64_t d = a.d;
 #pragma unroll
     for (int j = 0; j < kHC; ++j) in.x[j].to(xs[j]);
     if constexpr (kPost) {
-        Vec8<kBf16> fv, x1[kHC];
+        Vec8<false> fv, x1[kHC];
         in.f.to(fv);
-        expand8<kBf16>(fv, xs, co.pk, co.cm, x1);
+        expand8<false>(fv, xs, co.pk, co.cm, x1);
 #pragma unroll
         for (int k = 0; k < kHC; ++k) {
             if (live) x1[k].store(a.streams_out, (t * kHC + k) * d + e);
@@ -529,7 +473,7 @@ __device__ __forceinline__ void step_elementwise(const PassArgs& a, const StepDa
         }
     }
     if constexpr (kPre) {
-        Vec8<kBf16> yv;
+        Vec8<false> yv;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             float s = 0.f;
@@ -548,12 +492,11 @@ __device__ __forceinline__ void step_elementwise(const PassArgs& a, const StepDa
 
 // The sweep: workgroup = 4 waves x kTiles tiles of 16 tokens. Per 32-channel step,
 // each lane loads its tiles' stream values, fetches the next step's weights (L2)
-// before doing the step's work, and after the step's MFMAs splits those weights
-// into the other LDS buffer; one barrier per step. Every B fragment read from LDS
-// feeds all kTiles tiles of the wave.
-template <bool kBf16, bool kPost, bool kPre>
+// before doing the step's work, and after the step's MFMAs copies those weights
+// into the other LDS buffer; one barrier per step.
+template <bool kPost, bool kPre>
 __global__ __launch_bounds__(kPassBlock) void pass_kernel(PassArgs a) {
-    __shared__ PassLds<kBf16> lds;
+    __shared__ PassLds lds;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -567,17 +510,9 @@ __global__ __launch_bounds__(kPassBlock) void pass_kernel(PassArgs a) {
     const int c_end = min(a.nchunks, c_begin + a.chunks_per_split);
 
     // the B columns 24..31 (tile 1, columns 8..15) stay zero for the whole sweep
-    if constexpr (kBf16) {
-        for (int z = threadIdx.x; z < 2 * 3 * kHC * 4 * 8; z += kPassBlock) {
-            const int col = 8 + (z & 7), gg = (z >> 3) & 3, j = (z >> 5) & 3, term = (z >> 7) % 3,
-                      buf = z / (3 * kHC * 4 * 8);
-            lds.b[buf][b_slot(term, 1, j, gg * 16 + col)] = make_uint4(0, 0, 0, 0);
-        }
-    } else {
-        for (int z = threadIdx.x; z < 2 * 8 * kF32Row; z += kPassBlock) {
-            const int buf = z / (8 * kF32Row), o = z - buf * 8 * kF32Row;
-            lds.w[buf][kMix * kF32Row + o] = 0.f;
-        }
+    for (int z = threadIdx.x; z < 2 * 8 * kF32Row; z += kPassBlock) {
+        const int buf = z / (8 * kF32Row), o = z - buf * 8 * kF32Row;
+        lds.w[buf][kMix * kF32Row + o] = 0.f;
     }
 
     int64_t t[kTiles];
@@ -597,7 +532,7 @@ __global__ __launch_bounds__(kPassBlock) void pass_kernel(PassArgs a) {
     if (c_begin < c_end) {
         float4 w0[kStageLoads];
         fetch_weights(w0, a.hc_fn, d, c_begin);
-        commit_weights<kBf16>(kBf16 ? (void*)lds_b(lds, 0) : (void*)lds_w(lds, 0), w0);
+        commit_weights(lds.w[0], w0);
     }
     __syncthreads();
 
@@ -607,30 +542,16 @@ __global__ __launch_bounds__(kPassBlock) void pass_kernel(PassArgs a) {
         float4 wnext[kStageLoads];
         if (more) fetch_weights(wnext, a.hc_fn, d, ci + 1);   // L2, committed after the MFMAs
         const int64_t e = (int64_t)ci * kChunk + g * 8;
-        StepData<kBf16, kPost> in[kTiles];
+        StepData<kPost> in[kTiles];
 #pragma unroll
-        for (int q = 0; q < kTiles; ++q) load_step<kBf16, kPost>(in[q], a, t[q], tok_ok[q] && e < d, e);
+        for (int q = 0; q < kTiles; ++q) load_step<kPost>(in[q], a, t[q], tok_ok[q] && e < d, e);
 
-        Vec8<kBf16> xs[kTiles][kHC];
+        Vec8<false> xs[kTiles][kHC];
 #pragma unroll
         for (int q = 0; q < kTiles; ++q)
-            step_elementwise<kBf16, kPost, kPre>(a, in[q], co[q], t[q], tok_ok[q] && e < d, e, xs[q], sumsq[q]);
+            step_elementwise<kPost, kPre>(a, in[q], co[q], t[q], tok_ok[q] && e < d, e, xs[q], sumsq[q]);
 
-        if constexpr (kBf16) {
-            const uint4* B = lds.b[buf];
-#pragma unroll
-            for (int j = 0; j < kHC; ++j)
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                    for (int term = 0; term < 3; ++term) {
-                        const bf16x8_t Bv = __builtin_bit_cast(bf16x8_t, B[b_slot(term, nt, j, lane)]);
-#pragma unroll
-                        for (int q = 0; q < kTiles; ++q)
-                            acc[q][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                __builtin_bit_cast(bf16x8_t, xs[q][j].raw), Bv, acc[q][nt], 0, 0, 0);
-                    }
-        } else {
+        {
             // lane (r, g): A = token r, channel g*8 + c; B = mix nt*16 + r, same channel
             const float* W = lds.w[buf];
 #pragma unroll
@@ -650,7 +571,7 @@ __global__ __launch_bounds__(kPassBlock) void pass_kernel(PassArgs a) {
                 }
         }
         // the other buffer was last read before the previous barrier
-        if (more) commit_weights<kBf16>(kBf16 ? (void*)lds_b(lds, buf ^ 1) : (void*)lds_w(lds, buf ^ 1), wnext);
+        if (more) commit_weights(lds.w[buf ^ 1], wnext);
         __syncthreads();
     }
 
@@ -766,49 +687,8 @@ __global__ __launch_bounds__(kFinBlock) void finalize_kernel(FinalizeArgs f) {
     finalize16(f, ((int64_t)blockIdx.x * kFinBlock + threadIdx.x) >> 4, threadIdx.x & 15);
 }
 
-// ------------------------------------------------- bf16 sweep (stream-stationary)
-// Loading in the MFMA operand layout (16 token rows x 64 B per instruction) caps
-// reads at ~3.9 TB/s on MI355X, while 256-byte row runs reach ~5.8 TB/s, so
-// streams are loaded rowwise and transposed through LDS:
-//   - workgroup = 4 waves x 16 tokens; super-step = 128 channels. Lane
-//     (sub = lane/16, ch = lane%16) of wave w loads, for token group G (4 per
-//     wave) and stream j, 16 B at token 16w + 4G + sub, channels cs + 8ch: one
-//     instruction = 4 tokens x 256 B. Expand / collapse / sum of squares run in
-//     that layout (stores are 256 B runs too).
-//   - every wave writes its rounded values, all 4 streams, into the shared LDS
-//     A region in MFMA A layout (row = token, k-group = 8 channels),
-//     XOR-swizzled so that writes and reads are free of bank conflicts.
-//   - in the MFMA phase wave w owns stream j = w for all 64 tokens (4 row tiles).
-//     Its B operands come from L2, one 16-byte load per lane each, from weights
-//     split once per call (pack_weights_kernel) into three bf16 terms (hi + mid
-//     + lo, ~24 significant bits). The 24 mix columns take 5 MFMAs per tile and
-//     k-block (no zero padding): column tile 0 = mixes 0..15 (hi, mid, lo into
-//     one accumulator); column tile 1 = [hi | mid] of mixes 16..23, then [lo | 0]
-//     of mixes 16..23 into the same accumulator, whose two 8-column halves are
-//     added once at the end. A sixth MFMA multiplies the A tile by itself: since
-//     the A and B lane layouts coincide, mfma(A, A) accumulates the tile's Gram
-//     matrix, whose diagonal is each token's sum of squares. The 4 waves'
-//     partial results (one stream each) are summed through LDS.
-//   - two barriers per super-step; the next super-step's stream loads are issued
-//     before the MFMA phase, so they overlap it.
-constexpr int kSuper = 128;              // channels per super-step
-constexpr int kKbPerSuper = kSuper / kChunk;
-constexpr int kCoefF4 = 6;               // float4 per token: post_prev, comb_prev x4, pre_mix
+// ------------------------------------------------- bf16 projection weights
 constexpr int kFragsPerKb = 5;           // B operands per (stream, k-block): hi0 mid0 lo0 [hi1|mid1] [lo1|0]
-
-struct Sweep2Lds {
-    uint4 a[kHC * kKbPerSuper * 4 * 64];   // [stream][k-block][row tile][lane], 64 KB
-    float4 coef[kTokWG][kCoefF4];         // 6 KB
-};
-
-// Swizzled A slot: slot = ((j*4 + kb)*4 + tile)*64 + g*16 + r. The low 3 bits are
-// XORed with (g + 4*(kb & 1)): a transposing write (lanes with the same token
-// group and stream spread over 2 k-blocks x 4 k-groups) and a lane-ordered read
-// both touch 8 distinct bank groups per 8 lanes.
-__device__ __forceinline__ int a2_slot(int j, int kb, int tile, int lane) {
-    const int slot = ((j * kKbPerSuper + kb) * 4 + tile) * 64 + lane;
-    return slot ^ (((lane >> 4) + 4 * (kb & 1)) & 7);
-}
 
 // Splits 8 fp32 weights into three bf16 terms (w ~ hi + mid + lo).
 __device__ __forceinline__ void split3(const float4& a, const float4& b, uint4& hi, uint4& mid, uint4& lo) {
@@ -866,215 +746,255 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const float* __restri
     dst[4 * 64] = make_uint4(lo_half ? l1.x : 0u, lo_half ? l1.y : 0u, lo_half ? l1.z : 0u, lo_half ? l1.w : 0u);
 }
 
+// ------------------------------------------------ bf16 sweep: shared pieces
+// The bf16 sweep walks a channel slice in steps of 64 channels (two 32-channel
+// k-blocks). In its rowwise role lane (t8 = lane/8, c8 = lane%8) of wave w owns
+// token 8w + t8 and channels cs + 8*c8 .. +8 of step cs, in all 4 streams and in
+// the sublayer output: one 16-byte load per stream, one instruction = 8 tokens x
+// 128 B. Expanded / collapsed values are written, XOR-swizzled, into an LDS A
+// region from which the MFMA role reads 16-token x 32-channel operands.
+constexpr int kStep = 64;                                  // channels per step
+constexpr int kStepKb = kStep / kChunk;                     // k-blocks per step
+
+
+// A slot of (token t, stream j, 8-channel group q): rows (t, j) of 128 B; the
+// stream index is XORed with t's parity and the group with (t/2) % 8, so that an
+// MFMA A read (16 consecutive tokens at one group) and a rowwise write (2 tokens
+// x 8 groups per 16 lanes) each cover the 16 bank groups of a 256-byte window.
+__device__ __forceinline__ int a_slot(int t, int j, int q) {
+    return ((t * kHC + (j ^ (t & 1))) << 3) + (q ^ ((t >> 1) & 7));
+}
+
+template <bool kPost>
+struct StepRegs {
+    uint4 x[kHC];   // 8 channels of each stream
+    uint4 f;        // 8 channels of the sublayer output (expand only)
+};
+
+// ------------------------------------------------------------ bf16 sweep
+// Workgroup = 8 waves x 8 tokens = 64 tokens (four 16-token MFMA row tiles) x one
+// channel slice, walked in steps of 64 channels (two 32-channel k-blocks); one
+// workgroup per CU.
+//   - rowwise role (see above); the stream loads run two steps ahead in three
+//     register sets.
+//   - MFMA role: wave w multiplies stream j = w % 4 for k-block w / 4 of the step
+//     across all four row tiles, so every weight operand fetched from L2 serves
+//     64 tokens. Its 5 B operands are double-buffered and issued one step ahead,
+//     before that step's stream loads: vmcnt retires in issue order, so waiting
+//     for the weights only waits for loads at least two steps old.
+//   - the step loop is unrolled by six (three stream sets x two weight sets) so
+//     every set keeps fixed registers.
+constexpr int kSwWaves = 8;
+constexpr int kSwBlock = kSwWaves * 64;
+constexpr int kSwTok = 64;
+constexpr int kSwASlots = kSwTok * kHC * (kStep / 8);     // 16-byte slots per A buffer (32 KB)
+constexpr int kSweepTargetGroups = 256;   // one workgroup per CU
+
+struct SweepLds {
+    uint4 a[2][kSwASlots];                 // 64 KB; reused for the cross-wave reduction
+    float ss[kSwWaves][4][16];             // Gram diagonals per wave and tile
+};
+
 template <bool kPost, bool kPre>
-__global__ __launch_bounds__(kPassBlock, 2) void sweep2_kernel(PassArgs a, const uint4* __restrict__ packed) {
-    static_assert(kTokWave == 16 && kWaves == kHC, "one 16-token tile and one stream per wave");
-    __shared__ Sweep2Lds lds;
+__global__ __launch_bounds__(kSwBlock) void bf16_sweep_kernel(PassArgs a, const uint4* __restrict__ packed) {
+    __shared__ SweepLds lds;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int sub = lane >> 4, ch = lane & 15;   // rowwise role
+    const int mj = wave & 3, mkk = wave >> 2;    // MFMA role: stream, k-block of the step
+    const int t8 = lane >> 3, c8 = lane & 7;     // rowwise role
     const int64_t n = a.n, d = a.d;
     const int nkb = a.nchunks;
     const int split = (int)(blockIdx.x % (unsigned)a.nsplit);
     const int64_t group = blockIdx.x / (unsigned)a.nsplit;
-    const int64_t tbase = group * kTokWG + wave * kTokWave;   // this wave's rowwise tokens
+    const int64_t tok0 = group * kSwTok;
+    const int tl = wave * 8 + t8;
+    const bool tok_ok = tok0 + tl < n;
     const int kb_begin = split * a.chunks_per_split;
     const int kb_end = min(nkb, kb_begin + a.chunks_per_split);
+    const int64_t c_begin = (int64_t)kb_begin * kChunk;
+    const int64_t c_end = min(d, (int64_t)kb_end * kChunk);
+    const int nst = (int)((c_end - c_begin + kStep - 1) / kStep);   // >= 1: slices are never empty
 
-    for (int z = threadIdx.x; z < kTokWG * kCoefF4; z += kPassBlock) {
-        const int tl = z / kCoefF4, q = z - tl * kCoefF4;
-        const int64_t tt = group * kTokWG + tl;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (tt < n) {
-            if (kPost && q == 0) v = reinterpret_cast<const float4*>(a.post_prev)[tt];
-            if (kPost && q >= 1 && q <= 4) v = reinterpret_cast<const float4*>(a.comb_prev)[tt * 4 + q - 1];
-            if (kPre && q == 5) v = reinterpret_cast<const float4*>(a.pre_mix)[tt];
+    float pk[kHC], cm[kHC * kHC], pim[kHC];
+#pragma unroll
+    for (int i = 0; i < kHC; ++i) pk[i] = pim[i] = 0.f;
+#pragma unroll
+    for (int i = 0; i < kHC * kHC; ++i) cm[i] = 0.f;
+    if (tok_ok) {
+        const int64_t t = tok0 + tl;
+        if constexpr (kPost) {
+            const float4 pv = reinterpret_cast<const float4*>(a.post_prev)[t];
+            pk[0] = pv.x; pk[1] = pv.y; pk[2] = pv.z; pk[3] = pv.w;
+#pragma unroll
+            for (int j = 0; j < kHC; ++j) {
+                const float4 cv = reinterpret_cast<const float4*>(a.comb_prev)[t * kHC + j];
+                cm[4 * j] = cv.x; cm[4 * j + 1] = cv.y; cm[4 * j + 2] = cv.z; cm[4 * j + 3] = cv.w;
+            }
         }
-        lds.coef[tl][q] = v;
+        if constexpr (kPre) {
+            const float4 pv = reinterpret_cast<const float4*>(a.pre_mix)[t];
+            pim[0] = pv.x; pim[1] = pv.y; pim[2] = pv.z; pim[3] = pv.w;
+        }
     }
 
-    // buffer resources based at the wave's first token; ranges end at token n
-    const int64_t row_x = kHC * d * 2, row_f = d * 2;   // bytes per token
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(static_cast<const char*>(a.res) + tbase * row_x, (n - tbase) * row_x);
-    const __amdgpu_buffer_rsrc_t rf = make_rsrc(kPost ? static_cast<const char*>(a.f) + tbase * row_f : nullptr,
-                                                kPost ? (n - tbase) * row_f : 0);
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(kPost ? static_cast<char*>(a.streams_out) + tbase * row_x : nullptr,
-                                                kPost ? (n - tbase) * row_x : 0);
-    const __amdgpu_buffer_rsrc_t ry = make_rsrc(kPre ? static_cast<char*>(a.y) + tbase * row_f : nullptr,
-                                                kPre ? (n - tbase) * row_f : 0);
+    const int64_t row_x = kHC * d * 2, row_f = d * 2;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(static_cast<const char*>(a.res) + tok0 * row_x, (n - tok0) * row_x);
+    const __amdgpu_buffer_rsrc_t rf = make_rsrc(kPost ? static_cast<const char*>(a.f) + tok0 * row_f : nullptr,
+                                                kPost ? (n - tok0) * row_f : 0);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(kPost ? static_cast<char*>(a.streams_out) + tok0 * row_x : nullptr,
+                                                kPost ? (n - tok0) * row_x : 0);
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(kPre ? static_cast<char*>(a.y) + tok0 * row_f : nullptr,
+                                                kPre ? (n - tok0) * row_f : 0);
     const __amdgpu_buffer_rsrc_t rp = make_rsrc(packed, (int64_t)kHC * nkb * kFragsPerKb * 64 * 16);
-    const uint32_t lane_x = (uint32_t)(sub * row_x + ch * 16);
-    const uint32_t lane_f = (uint32_t)(sub * row_f + ch * 16);
+    const uint32_t lane_x = tok_ok ? (uint32_t)(tl * row_x + c8 * 16) : kOffMasked;
+    const uint32_t lane_f = tok_ok ? (uint32_t)(tl * row_f + c8 * 16) : kOffMasked;
     const uint32_t lane_p = (uint32_t)(lane * 16);
-    const int g = lane >> 4, col = lane & 15;   // MFMA role: k-group, column
+
+    auto load_step = [&](StepRegs<kPost>& R, int s) {
+        const int64_t cs = c_begin + (int64_t)s * kStep;
+        const bool ok = cs + c8 * 8 < c_end;
+        const uint32_t vx = ok ? lane_x : kOffMasked, vf = ok ? lane_f : kOffMasked;
+        const uint32_t so = (uint32_t)(cs * 2);
+#pragma unroll
+        for (int j = 0; j < kHC; ++j) R.x[j] = buf_load16(rx, vx, so + (uint32_t)(j * row_f));
+        if constexpr (kPost) R.f = buf_load16(rf, vf, so);
+    };
+    // the 5 B operands of (stream mj, k-block mkk of step s); past the slice: zeros
+    auto load_b = [&](uint4 (&B)[kFragsPerKb], int s) {
+        const int kb = kb_begin + s * kStepKb + mkk;
+        const uint32_t v = kb < kb_end ? lane_p : kOffMasked;
+#pragma unroll
+        for (int q = 0; q < kFragsPerKb; ++q)
+            B[q] = buf_load16(rp, v, (uint32_t)((((int64_t)mj * nkb + kb) * kFragsPerKb + q) * 64 * 16));
+    };
 
     floatx4_t acc[4][2], gram[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc[q][0] = acc[q][1] = gram[q] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int T = 0; T < 4; ++T) acc[T][0] = acc[T][1] = gram[T] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-    Raw8<true> X[4][kHC], F[4];
-    auto load_x = [&](int kb0) {
-        const int64_t cs = (int64_t)kb0 * kChunk, c = cs + ch * 8;
-        const bool c_ok = c < d && c < (int64_t)kb_end * kChunk;
+    auto step = [&](int s, StepRegs<kPost>& cur, StepRegs<kPost>& ahead, uint4 (&Bcur)[kFragsPerKb],
+                    uint4 (&Bnext)[kFragsPerKb]) {
+        load_b(Bnext, s + 1);
+        load_step(ahead, s + 2);
+        const int64_t cs = c_begin + (int64_t)s * kStep;
+        const bool ok = cs + c8 * 8 < c_end;
+        const uint32_t vx = ok ? lane_x : kOffMasked, vf = ok ? lane_f : kOffMasked;
+        const uint32_t so = (uint32_t)(cs * 2);
+        uint32_t yw[4];
 #pragma unroll
-        for (int G = 0; G < 4; ++G) {
-            const bool live = c_ok && tbase + 4 * G + sub < n;   // masked lanes read zeros
-            const uint32_t vx = live ? lane_x : kOffMasked, vf = live ? lane_f : kOffMasked;
+        for (int w = 0; w < 4; ++w) {
+            uint32_t xw[kHC];
 #pragma unroll
-            for (int j = 0; j < kHC; ++j)
-                X[G][j].w = buf_load16(rx, vx, (uint32_t)((4 * G * kHC + j) * row_f + cs * 2));
-            if constexpr (kPost) F[G].w = buf_load16(rf, vf, (uint32_t)(4 * G * row_f + cs * 2));
-        }
-    };
-    // B operands of the next k-block to multiply (one k-block ahead, carried
-    // across super-steps so the elementwise phase hides their latency)
-    uint4 Bf[kFragsPerKb];
-    auto load_b = [&](int kbg) {
-        if (kbg < kb_end) {
-#pragma unroll
-            for (int q = 0; q < kFragsPerKb; ++q)
-                Bf[q] = buf_load16(rp, lane_p, (uint32_t)((((int64_t)wave * nkb + kbg) * kFragsPerKb + q) * 64 * 16));
-        }
-    };
-    if (kb_begin < kb_end) load_x(kb_begin);
-    load_b(kb_begin);
-    __syncthreads();   // coefficients
-
-    for (int kb0 = kb_begin; kb0 < kb_end; kb0 += kKbPerSuper) {
-        const int64_t cs = (int64_t)kb0 * kChunk, c = cs + ch * 8;
-        const bool c_ok = c < d && c < (int64_t)kb_end * kChunk;
-        // expand / collapse / sum of squares, rowwise, two channels (one packed
-        // word per stream) at a time; results into the A region
-#pragma unroll
-        for (int G = 0; G < 4; ++G) {
-            const bool live = c_ok && tbase + 4 * G + sub < n;
-            const uint32_t vx = live ? lane_x : kOffMasked, vf = live ? lane_f : kOffMasked;
-            const float4* cf = lds.coef[wave * kTokWave + 4 * G + sub];
-            float pk[kHC], cm[kHC * kHC], pim[kHC];
+            for (int j = 0; j < kHC; ++j) xw[j] = (&cur.x[j].x)[w];
             if constexpr (kPost) {
-                const float4 pv = cf[0];
-                pk[0] = pv.x; pk[1] = pv.y; pk[2] = pv.z; pk[3] = pv.w;
+                const uint32_t fw = (&cur.f.x)[w];
+                const float f0 = bf16_lo(fw), f1 = bf16_hi(fw);
+                uint32_t ow[kHC];
 #pragma unroll
-                for (int j = 0; j < kHC; ++j) {
-                    const float4 cv = cf[1 + j];
-                    cm[4 * j] = cv.x; cm[4 * j + 1] = cv.y; cm[4 * j + 2] = cv.z; cm[4 * j + 3] = cv.w;
-                }
-            }
-            if constexpr (kPre) {
-                const float4 pv = cf[5];
-                pim[0] = pv.x; pim[1] = pv.y; pim[2] = pv.z; pim[3] = pv.w;
-            }
-            uint32_t yw[4];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                uint32_t xw[kHC];
-#pragma unroll
-                for (int j = 0; j < kHC; ++j) xw[j] = (&X[G][j].w.x)[w];
-                if constexpr (kPost) {
-                    const uint32_t fw = (&F[G].w.x)[w];
-                    const float f0 = bf16_lo(fw), f1 = bf16_hi(fw);
-                    uint32_t ow[kHC];
-#pragma unroll
-                    for (int k = 0; k < kHC; ++k) {
-                        float o0 = pk[k] * f0, o1 = pk[k] * f1;
-#pragma unroll
-                        for (int j = 0; j < kHC; ++j) {
-                            o0 = fmaf(cm[4 * j + k], bf16_lo(xw[j]), o0);
-                            o1 = fmaf(cm[4 * j + k], bf16_hi(xw[j]), o1);
-                        }
-                        ow[k] = pack_bf16x2(o0, o1);
-                    }
-#pragma unroll
-                    for (int k = 0; k < kHC; ++k) xw[k] = (&X[G][k].w.x)[w] = ow[k];
-                }
-                if constexpr (kPre) {
-                    float y0 = 0.f, y1 = 0.f;
+                for (int k = 0; k < kHC; ++k) {
+                    float o0 = pk[k] * f0, o1 = pk[k] * f1;
 #pragma unroll
                     for (int j = 0; j < kHC; ++j) {
-                        y0 = fmaf(pim[j], bf16_lo(xw[j]), y0);
-                        y1 = fmaf(pim[j], bf16_hi(xw[j]), y1);
+                        o0 = fmaf(cm[4 * j + k], bf16_lo(xw[j]), o0);
+                        o1 = fmaf(cm[4 * j + k], bf16_hi(xw[j]), o1);
                     }
-                    yw[w] = pack_bf16x2(y0, y1);
+                    ow[k] = pack_bf16x2(o0, o1);
                 }
-            }
-            if constexpr (kPost) {
 #pragma unroll
-                for (int k = 0; k < kHC; ++k)
-                    buf_store16(X[G][k].w, ro, vx, (uint32_t)((4 * G * kHC + k) * row_f + cs * 2));
+                for (int k = 0; k < kHC; ++k) xw[k] = (&cur.x[k].x)[w] = ow[k];
             }
-            if constexpr (kPre)
-                buf_store16(make_uint4(yw[0], yw[1], yw[2], yw[3]), ry, vf, (uint32_t)(4 * G * row_f + cs * 2));
-            // A layout: tile = wave, row = 4G + sub, k-block = ch / 4, k-group = ch % 4
+            if constexpr (kPre) {
+                float y0 = 0.f, y1 = 0.f;
 #pragma unroll
-            for (int j = 0; j < kHC; ++j)
-                lds.a[a2_slot(j, ch >> 2, wave, (ch & 3) * 16 + 4 * G + sub)] = X[G][j].w;
-            __builtin_amdgcn_sched_barrier(0);
+                for (int j = 0; j < kHC; ++j) {
+                    y0 = fmaf(pim[j], bf16_lo(xw[j]), y0);
+                    y1 = fmaf(pim[j], bf16_hi(xw[j]), y1);
+                }
+                yw[w] = pack_bf16x2(y0, y1);
+            }
         }
-        // next super-step's streams: in flight during the MFMA phase
-        if (kb0 + kKbPerSuper < kb_end) load_x(kb0 + kKbPerSuper);
-        __syncthreads();   // A region complete
+        if constexpr (kPost) {
+#pragma unroll
+            for (int k = 0; k < kHC; ++k) buf_store16(cur.x[k], ro, vx, so + (uint32_t)(k * row_f));
+        }
+        if constexpr (kPre) buf_store16(make_uint4(yw[0], yw[1], yw[2], yw[3]), ry, vf, so);
+        uint4* A = lds.a[s & 1];
+#pragma unroll
+        for (int j = 0; j < kHC; ++j) A[a_slot(tl, j, c8)] = cur.x[j];
+        __syncthreads();   // A buffer complete; the other buffer is free again
+#pragma unroll
+        for (int T = 0; T < 4; ++T) {
+            const bf16x8_t Av =
+                __builtin_bit_cast(bf16x8_t, A[a_slot(T * 16 + (lane & 15), mj, mkk * 4 + (lane >> 4))]);
+#pragma unroll
+            for (int q = 0; q < kFragsPerKb; ++q)
+                acc[T][q < 3 ? 0 : 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    Av, __builtin_bit_cast(bf16x8_t, Bcur[q]), acc[T][q < 3 ? 0 : 1], 0, 0, 0);
+            gram[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, Av, gram[T], 0, 0, 0);
+        }
+    };
 
-        // MFMA phase: stream j = wave, 4 row tiles, the super-step's k-blocks; once a
-        // k-block's MFMAs are issued its B registers take the next k-block
-#pragma unroll 1
-        for (int k = 0; k < kKbPerSuper; ++k) {
-            const int kbg = kb0 + k;
-            if (kbg >= kb_end) break;   // uniform
-#pragma unroll
-            for (int tile = 0; tile < 4; ++tile) {
-                const bf16x8_t A = __builtin_bit_cast(bf16x8_t, lds.a[a2_slot(wave, k, tile, lane)]);
-#pragma unroll
-                for (int q = 0; q < kFragsPerKb; ++q)
-                    acc[tile][q < 3 ? 0 : 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        A, __builtin_bit_cast(bf16x8_t, Bf[q]), acc[tile][q < 3 ? 0 : 1], 0, 0, 0);
-                gram[tile] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, A, gram[tile], 0, 0, 0);
-            }
-            load_b(kbg + 1);
-        }
-        __syncthreads();   // A region consumed
+    StepRegs<kPost> R0, R1, R2;
+    uint4 B0[kFragsPerKb], B1[kFragsPerKb];
+    load_b(B0, 0);
+    load_step(R0, 0);
+    load_step(R1, 1);
+    // every exit leaves the loop: the back edge is only reached after all six
+    // steps, so the loads pending at the loop head are always the same sets
+    for (int s = 0;; s += 6) {
+        step(s, R0, R2, B0, B1);
+        if (s + 1 >= nst) break;
+        step(s + 1, R1, R0, B1, B0);
+        if (s + 2 >= nst) break;
+        step(s + 2, R2, R1, B0, B1);
+        if (s + 3 >= nst) break;
+        step(s + 3, R0, R2, B1, B0);
+        if (s + 4 >= nst) break;
+        step(s + 4, R1, R0, B0, B1);
+        if (s + 5 >= nst) break;
+        step(s + 5, R2, R1, B1, B0);
+        if (s + 6 >= nst) break;
     }
 
-    float* part = a.part + (int64_t)split * n * kPart;
-    // column tile 1: mixes 16 + c = columns c ([hi | lo] part) + c + 8 ([mid] part)
+    __syncthreads();   // every wave is done with the A buffers
 #pragma unroll
-    for (int tile = 0; tile < 4; ++tile)
+    for (int T = 0; T < 4; ++T)
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) acc[tile][1][ii] += dpp<kRowRor8>(acc[tile][1][ii]);
-    // partial projections and sums of squares (Gram diagonal: row 4g + ii sits in
-    // column 4g + ii) of the 4 streams: sum over waves through LDS
-    float* red = reinterpret_cast<float*>(lds.a);   // [wave][tile][nt][ii][lane], 32 KB
-    float* red_ss = red + kWaves * 2048;            // [wave][tile][row], 1 KB
+        for (int ii = 0; ii < 4; ++ii) acc[T][1][ii] += dpp<kRowRor8>(acc[T][1][ii]);
+    const int g = lane >> 4, col = lane & 15;
+    float* red = reinterpret_cast<float*>(&lds.a[0][0]);   // [wave][T][nt][ii][lane], 64 KB
 #pragma unroll
-    for (int tile = 0; tile < 4; ++tile)
+    for (int T = 0; T < 4; ++T)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) red[(((wave * 4 + tile) * 2 + nt) * 4 + ii) * 64 + lane] = acc[tile][nt][ii];
+            for (int ii = 0; ii < 4; ++ii) red[(((wave * 4 + T) * 2 + nt) * 4 + ii) * 64 + lane] = acc[T][nt][ii];
 #pragma unroll
-    for (int tile = 0; tile < 4; ++tile)
+    for (int T = 0; T < 4; ++T)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii)
-            if (col == 4 * g + ii) red_ss[(wave * 4 + tile) * 16 + col] = gram[tile][ii];
+            if (col == 4 * g + ii) lds.ss[wave][T][col] = gram[T][ii];
     __syncthreads();
-    for (int e = threadIdx.x; e < 4 * 2 * 4 * 64; e += kPassBlock) {
-        const int l = e & 63, ii = (e >> 6) & 3, nt = (e >> 8) & 1, tile = e >> 9;
+    float* part = a.part + (int64_t)split * n * kPart;
+    for (int e = threadIdx.x; e < 4 * 2 * 4 * 64; e += kSwBlock) {
+        const int l = e & 63, ii = (e >> 6) & 3, nt = (e >> 8) & 1, T = e >> 9;
         const int mix = nt * 16 + (l & 15);
-        const int64_t t = group * kTokWG + tile * 16 + 4 * (l >> 4) + ii;
+        const int64_t t = tok0 + T * 16 + 4 * (l >> 4) + ii;
         if (mix < kMix && t < n) {
             float s = 0.f;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) s += red[w * 2048 + e];
+            for (int w = 0; w < kSwWaves; ++w) s += red[w * 2048 + e];
             part[t * kPart + mix] = s;
         }
     }
-    if (threadIdx.x < kTokWG) {   // token tile*16 + row of the group
-        const int tile = threadIdx.x >> 4, row = threadIdx.x & 15;
-        const int64_t t = group * kTokWG + threadIdx.x;
+    if (threadIdx.x < kSwTok) {   // token T*16 + row of the group
+        const int T = threadIdx.x >> 4, row = threadIdx.x & 15;
+        const int64_t t = tok0 + threadIdx.x;
         if (t < n) {
             float s = 0.f;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) s += red_ss[(w * 4 + tile) * 16 + row];
+            for (int w = 0; w < kSwWaves; ++w) s += lds.ss[w][T][row];
             part[t * kPart + kMix] = s;
         }
     }
@@ -1085,24 +1005,34 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 }  // namespace
 
 // ------------------------------------------------------------------- launchers
-PassPlan plan_pass(int64_t n, int64_t d) {
+constexpr int kF32Unit = 128;   // pass_kernel slices are whole 128-channel units
+
+PassPlan plan_pass(int64_t n, int64_t d, bool bf16) {
     PassPlan p{};
-    p.tiles = ceil_div(n, kTokWG);
+    // bf16 sweep: 64-token groups, slices of whole 64-channel steps, ~256
+    // workgroups (one per CU); fp32 pass_kernel: 64-token tiles, 128-channel units
+    const int tok = bf16 ? kSwTok : kTokWG;
+    const int unit = bf16 ? kStep : kF32Unit;
+    p.tiles = ceil_div(n, tok);
     p.nchunks = (int)ceil_div(d, kChunk);
-    // channel slices are whole 128-channel super-steps (the bf16 sweep's unit)
-    const int nsuper = (int)ceil_div(d, kSuper);
-    const int64_t target_groups = HC_TARGET_GROUPS;
+    const int nunits = (int)ceil_div(d, unit);
+    const int64_t target_groups = bf16 ? kSweepTargetGroups : kPassTargetGroups;
     int64_t ns = ceil_div(target_groups, p.tiles > 0 ? p.tiles : 1);
     if (ns < 1) ns = 1;
-    if (ns > nsuper) ns = nsuper;
+    if (ns > nunits) ns = nunits;
     if (ns > 64) ns = 64;
-    p.chunks_per_split = (int)ceil_div(nsuper, ns) * kKbPerSuper;
+    p.chunks_per_split = (int)ceil_div(nunits, ns) * (unit / kChunk);
     p.nsplit = (int)ceil_div(p.nchunks, p.chunks_per_split);
     // [partial rows: nsplit x n x 32 floats][packed weights: 4 streams x nchunks x 5 x 1 KB]
     p.partial_bytes = (size_t)p.nsplit * (size_t)n * kPart * sizeof(float);
     p.packed_bytes = (size_t)kHC * (size_t)p.nchunks * kFragsPerKb * 64 * 16;
     p.workspace_bytes = p.partial_bytes + p.packed_bytes;
     return p;
+}
+
+size_t workspace_bytes(int64_t n, int64_t d) {
+    const PassPlan a = plan_pass(n, d, false), b = plan_pass(n, d, true);
+    return a.workspace_bytes > b.workspace_bytes ? a.workspace_bytes : b.workspace_bytes;
 }
 
 hipError_t launch_split(const float* mixes, const float* scale, const float* base, int64_t n, int iters,
@@ -1134,20 +1064,20 @@ hipError_t launch_post(const void* f, const void* res, bool bf16, const float* p
 
 namespace {
 template <bool kPost, bool kPre>
-void launch_sweep2_t(const PassArgs& a, const PassPlan& p, const uint4* packed, hipStream_t stream) {
-    hipLaunchKernelGGL((sweep2_kernel<kPost, kPre>), dim3((unsigned)(p.tiles * p.nsplit)), dim3(kPassBlock), 0,
+void launch_sweep_t(const PassArgs& a, const PassPlan& p, const uint4* packed, hipStream_t stream) {
+    hipLaunchKernelGGL((bf16_sweep_kernel<kPost, kPre>), dim3((unsigned)(p.tiles * p.nsplit)), dim3(kSwBlock), 0,
                        stream, a, packed);
 }
 
 template <bool kPost, bool kPre>
 void launch_pass_t(const PassArgs& a, const PassPlan& p, hipStream_t stream) {
-    hipLaunchKernelGGL((pass_kernel<false, kPost, kPre>), dim3((unsigned)(p.tiles * p.nsplit)), dim3(kPassBlock), 0,
+    hipLaunchKernelGGL((pass_kernel<kPost, kPre>), dim3((unsigned)(p.tiles * p.nsplit)), dim3(kPassBlock), 0,
                        stream, a);
 }
 }  // namespace
 
 hipError_t launch_pass_and_finalize(const PassRequest& r, hipStream_t stream) {
-    const PassPlan p = plan_pass(r.n, r.d);
+    const PassPlan p = plan_pass(r.n, r.d, r.bf16);
     PassArgs a{};
     a.res = r.res;
     a.f = r.f_prev;
@@ -1184,10 +1114,10 @@ hipError_t launch_pass_and_finalize(const PassRequest& r, hipStream_t stream) {
         uint4* packed = reinterpret_cast<uint4*>(static_cast<char*>(r.workspace) + p.partial_bytes);
         hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)ceil_div((int64_t)kHC * p.nchunks * 64, 256)),
                            dim3(256), 0, stream, r.hc_fn, r.d, p.nchunks, packed);
-        if (post && pre) launch_sweep2_t<true, true>(a, p, packed, stream);
-        else if (post) launch_sweep2_t<true, false>(a, p, packed, stream);
-        else if (pre) launch_sweep2_t<false, true>(a, p, packed, stream);
-        else launch_sweep2_t<false, false>(a, p, packed, stream);
+        if (post && pre) launch_sweep_t<true, true>(a, p, packed, stream);
+        else if (post) launch_sweep_t<true, false>(a, p, packed, stream);
+        else if (pre) launch_sweep_t<false, true>(a, p, packed, stream);
+        else launch_sweep_t<false, false>(a, p, packed, stream);
     } else {
         if (post && pre) launch_pass_t<true, true>(a, p, stream);
         else if (post) launch_pass_t<true, false>(a, p, stream);

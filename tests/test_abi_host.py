@@ -57,7 +57,7 @@ def test_version_and_status_strings():
 
 def test_workspace_size_rule():
     # [one 128-byte partial row per (channel slice, token); slices are whole
-    #  128-channel steps][the weights split into bf16 terms: 4 streams x
+    #  64- or 128-channel steps][the weights split into bf16 terms: 4 streams x
     #  ceil(d/32) k-blocks x 5 B operands x 1 KB]
     assert hc.workspace_size(0, 4, 5120) == 0
     assert hc.workspace_size(16, 3, 5120) == 0
@@ -67,7 +67,7 @@ def test_workspace_size_rule():
         part = ws - 4 * (-(-d // 32)) * 5 * 1024
         assert part > 0 and part % (128 * n) == 0
         nsplit = part // (128 * n)
-        assert 1 <= nsplit <= min(64, -(-d // 128))
+        assert 1 <= nsplit <= min(64, -(-d // 64))
 
 
 def _split(mixes=A, scale=B, base=C, n=16, hc_=4, iters=20, eps=1e-6, pre=A + 4096, post=A + 8192,
