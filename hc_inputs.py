@@ -146,10 +146,20 @@ def stress(seed: int = 0, rows: int = STRESS_ROWS, hc: int = HC, device="cpu"):
     return dict(mixes=logits, scale=scale, base=base, hot_rows=hot, hot_cols=col)
 
 
-def long_prefill_layer_params(seed: int, layers: int = 40, hc: int = HC, d: int = 5120,
-                              device="cpu"):
-    """Independent (attention, FFN) mix parameters for each of ``layers`` layers,
-    scale ~ U(0.5, 2)."""
-    g = generator(seed + 1, device)
-    return [(mix_params(g, hc, d, "uniform", device), mix_params(g, hc, d, "uniform", device))
-            for _ in range(layers)]
+def long_prefill(seed: int = 0, device="cpu", layers: int = 40, pool: int = 4, w: Workload = LONG_PREFILL):
+    """B=2, T=32768, d=5120, bf16 streams: independent (attention, FFN) mix
+    parameters for each of ``layers`` layers (scale ~ U(0.5, 2)), streams
+    x [n, 4, d] ~ N(0, 1), a pool of ``pool`` sublayer outputs [n, d] ~ N(0, 1)
+    that the chain's sublayers cycle through (sublayer k uses pool[k % pool]),
+    and the previous call whose pre weights collapse the first sublayer.
+
+    Draw order: layer parameters (attention, FFN per layer), streams, pool,
+    previous call. Sized for generation on the GPU (the fp32 draw of the streams
+    alone is 5.4 GB)."""
+    g = generator(seed, device)
+    params = [(mix_params(g, w.hc, w.d, "uniform", device), mix_params(g, w.hc, w.d, "uniform", device))
+              for _ in range(layers)]
+    x = streams(g, w.n, w.hc, w.d, w.dtype, device=device)
+    f_pool = [sublayer_output(g, w.n, w.d, w.dtype, device) for _ in range(pool)]
+    prev = previous_call(g, w.n, w.hc, device)
+    return dict(workload=w, params=params, x=x, f_pool=f_pool, prev=prev)

@@ -204,3 +204,43 @@ def test_fused_deterministic_and_zero_tokens():
     e = hc.hc_fused_step(xd[:0], *to_dev(inp["attn"]), pre_mix=pi[:0])
     sync()
     assert e["pre"].numel() == 0
+
+
+# ------------------------------------------------------- long prefill, 40 layers
+def test_long_prefill_40_layers_sampled_tokens():
+    """Long prefill (B=2, T=32768: 65,536 tokens, d=5120, bf16 streams): the 40
+    layers' attention and FFN boundaries chained at full size on the GPU, in the
+    order of Block.forward (80 fused steps, each expanding the previous sublayer's
+    output in place, then the last sublayer's expand), and 32 sampled tokens taken
+    through the same chain by the oracle from the same inputs. Each sublayer's
+    output is drawn from a pool of 4 buffers (sublayer k uses pool[k % 4])."""
+    inp = hc_inputs.long_prefill(seed=0, device=DEV)
+    x, pool, params = inp["x"], inp["f_pool"], inp["params"]
+    n = x.shape[0]
+    sample = torch.randperm(n, generator=hc_inputs.generator(7))[:32].sort().values
+    pi_all, _, _ = oracle.hc_split_sinkhorn(*(t.cpu() for t in inp["prev"]))
+    cpu_rows = lambda t: t[sample.to(t.device)].cpu()
+    ref_x = cpu_rows(x)
+    ref_pool = [cpu_rows(f) for f in pool]
+    ref_params = [tuple(tuple(t.cpu() for t in p) for p in layer) for layer in params]
+    print(f"  long prefill: n={n}, sampled tokens {sample[:4].tolist()}...", flush=True)
+
+    ws = torch.empty(hc.workspace_size(n, 4, x.shape[-1]), dtype=torch.uint8, device=DEV)
+    pi, post, comb, ref_pi, ref_post, ref_comb = pi_all.to(DEV), None, None, pi_all[sample], None, None
+    for k in range(2 * len(params)):
+        p_gpu, p_cpu = params[k // 2][k % 2], ref_params[k // 2][k % 2]
+        f_gpu = pool[(k - 1) % len(pool)] if k else None
+        f_cpu = ref_pool[(k - 1) % len(pool)] if k else None
+        r = hc.hc_fused_step(x, *p_gpu, pre_mix=pi, f_prev=f_gpu, post_prev=post, comb_prev=comb,
+                             streams_out=x if k else None, workspace=ws)
+        pi, post, comb, y = r["pre"], r["post"], r["comb"], r["y"]
+        ref = oracle.fused_step(ref_x, *p_cpu, pre_mix=ref_pi, f_prev=f_cpu, post_prev=ref_post, comb_prev=ref_comb)
+        ref_x, ref_pi, ref_post, ref_comb, ref_y = ref["streams"], ref["pre"], ref["post"], ref["comb"], ref["y"]
+    last = (2 * len(params) - 1) % len(pool)
+    hc.hc_post(pool[last], x, post, comb, out=x)
+    ref_x = oracle.hc_post(ref_pool[last], ref_x, ref_post, ref_comb)
+    sync()
+    check("final streams (sampled)", cpu_rows(x), ref_x, TOL_BF16)
+    check("last collapse (sampled)", cpu_rows(y), ref_y, TOL_BF16)
+    for name, g, rr in (("last pre", pi, ref_pi), ("last post", post, ref_post), ("last comb", comb, ref_comb)):
+        check(f"{name} (sampled)", cpu_rows(g), rr, TOL_BF16, rho=1.0)
