@@ -16,9 +16,7 @@ struct PassPlan {
     int nchunks;
     int chunks_per_split;
     int nsplit;
-    size_t partial_bytes;    // per-slice partial rows
-    size_t packed_bytes;     // weights split into bf16 terms (bf16 streams)
-    size_t workspace_bytes;  // partial_bytes + packed_bytes
+    size_t workspace_bytes;  // per-slice partial rows
 };
 PassPlan plan_pass(int64_t n, int64_t d, bool bf16);
 // Workspace that covers the plans of both stream dtypes.

@@ -11,7 +11,6 @@
 //   split_kernel        one lane per token: sigmoid split + Sinkhorn in registers.
 //   pre_kernel          collapse, one lane per (token, 8 channels), 128-bit loads.
 //   post_kernel         expand + combine, one lane per (token, 8 channels).
-//   pack_weights_kernel splits hc_fn into three bf16 terms in MFMA B layout.
 //   bf16_sweep_kernel   one pass over 64 tokens x a channel slice of bf16 streams:
 //                       optional expand (previous sublayer's post/comb), optional
 //                       collapse, and the partial 24-wide projection (MFMA) and
@@ -688,7 +687,11 @@ __global__ __launch_bounds__(kFinBlock) void finalize_kernel(FinalizeArgs f) {
 }
 
 // ------------------------------------------------- bf16 projection weights
-constexpr int kFragsPerKb = 5;           // B operands per (stream, k-block): hi0 mid0 lo0 [hi1|mid1] [lo1|0]
+// The 24 mix columns take 5 B operands per 32-channel k-block and stream:
+// hi, mid, lo of mixes 0..15 (one accumulator), then [hi | mid] and [lo | 0] of
+// mixes 16..23 (a second accumulator whose two 8-column halves are added at the
+// end).
+constexpr int kFragsPerKb = 5;
 
 // Splits 8 fp32 weights into three bf16 terms (w ~ hi + mid + lo).
 __device__ __forceinline__ void split3(const float4& a, const float4& b, uint4& hi, uint4& mid, uint4& lo) {
@@ -705,45 +708,6 @@ __device__ __forceinline__ void split3(const float4& a, const float4& b, uint4& 
     hi = make_uint4(h[0], h[1], h[2], h[3]);
     mid = make_uint4(m[0], m[1], m[2], m[3]);
     lo = make_uint4(l[0], l[1], l[2], l[3]);
-}
-
-// Packed weights: for stream j and 32-channel k-block kbg, 5 B operands of 64
-// lanes x 16 B in v_mfma_f32_16x16x32_bf16 layout (lane: k-group g = lane/16,
-// column col = lane%16, channels kbg*32 + 8g .. +8 of stream j):
-//   0, 1, 2: hi, mid, lo of row col (mixes 0..15)
-//   3: hi of row 16 + col (col < 8), mid of row 16 + col - 8 (col >= 8)
-//   4: lo of row 16 + col (col < 8), zero (col >= 8)
-// Channels >= d are zero. One thread per (j, kbg, lane).
-__global__ __launch_bounds__(256) void pack_weights_kernel(const float* __restrict__ W, int64_t d, int nkb,
-                                                           uint4* __restrict__ packed) {
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (gid >= (int64_t)kHC * nkb * 64) return;
-    const int lane = (int)(gid & 63);
-    const int64_t jk = gid >> 6;                                    // j * nkb + kbg
-    const int j = (int)(jk / nkb), kbg = (int)(jk - (int64_t)j * nkb);
-    const int g = lane >> 4, col = lane & 15;
-    const int64_t e0 = (int64_t)kbg * kChunk + g * 8;
-    float4 w0a = make_float4(0.f, 0.f, 0.f, 0.f), w0b = w0a, w1a = w0a, w1b = w0a;
-    if (e0 < d) {                                                   // d % 8 == 0: whole groups
-        const float4* r0 = reinterpret_cast<const float4*>(W + (int64_t)col * kHC * d + (int64_t)j * d + e0);
-        const float4* r1 =
-            reinterpret_cast<const float4*>(W + (int64_t)(16 + (col & 7)) * kHC * d + (int64_t)j * d + e0);
-        w0a = r0[0];
-        w0b = r0[1];
-        w1a = r1[0];
-        w1b = r1[1];
-    }
-    uint4 h0, m0, l0, h1, m1, l1;
-    split3(w0a, w0b, h0, m0, l0);
-    split3(w1a, w1b, h1, m1, l1);
-    uint4* dst = packed + jk * kFragsPerKb * 64 + lane;
-    dst[0 * 64] = h0;
-    dst[1 * 64] = m0;
-    dst[2 * 64] = l0;
-    const bool lo_half = col < 8;
-    dst[3 * 64] = make_uint4(lo_half ? h1.x : m1.x, lo_half ? h1.y : m1.y, lo_half ? h1.z : m1.z,
-                             lo_half ? h1.w : m1.w);
-    dst[4 * 64] = make_uint4(lo_half ? l1.x : 0u, lo_half ? l1.y : 0u, lo_half ? l1.z : 0u, lo_half ? l1.w : 0u);
 }
 
 // ------------------------------------------------ bf16 sweep: shared pieces
@@ -778,10 +742,13 @@ struct StepRegs {
 //   - rowwise role (see above); the stream loads run two steps ahead in three
 //     register sets.
 //   - MFMA role: wave w multiplies stream j = w % 4 for k-block w / 4 of the step
-//     across all four row tiles, so every weight operand fetched from L2 serves
-//     64 tokens. Its 5 B operands are double-buffered and issued one step ahead,
-//     before that step's stream loads: vmcnt retires in issue order, so waiting
-//     for the weights only waits for loads at least two steps old.
+//     across all four row tiles, so every weight fetched from L2 serves 64
+//     tokens. Its fp32 weights (8 channels of two mix rows per lane, 64 B) are
+//     double-buffered and issued one step ahead, before that step's stream
+//     loads: vmcnt retires in issue order, so waiting for the weights only waits
+//     for loads at least two steps old. After the barrier they are split into
+//     three bf16 terms (hi + mid + lo, ~24 significant bits) that form the 5 B
+//     operands; the split's VALU work hides under the memory-bound step.
 //   - the step loop is unrolled by six (three stream sets x two weight sets) so
 //     every set keeps fixed registers.
 constexpr int kSwWaves = 8;
@@ -796,7 +763,7 @@ struct SweepLds {
 };
 
 template <bool kPost, bool kPre>
-__global__ __launch_bounds__(kSwBlock) void bf16_sweep_kernel(PassArgs a, const uint4* __restrict__ packed) {
+__global__ __launch_bounds__(kSwBlock) void bf16_sweep_kernel(PassArgs a) {
     __shared__ SweepLds lds;
 
     const int lane = threadIdx.x & 63;
@@ -846,10 +813,15 @@ __global__ __launch_bounds__(kSwBlock) void bf16_sweep_kernel(PassArgs a, const 
                                                 kPost ? (n - tok0) * row_x : 0);
     const __amdgpu_buffer_rsrc_t ry = make_rsrc(kPre ? static_cast<char*>(a.y) + tok0 * row_f : nullptr,
                                                 kPre ? (n - tok0) * row_f : 0);
-    const __amdgpu_buffer_rsrc_t rp = make_rsrc(packed, (int64_t)kHC * nkb * kFragsPerKb * 64 * 16);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.hc_fn, (int64_t)kMix * kHC * d * 4);
     const uint32_t lane_x = tok_ok ? (uint32_t)(tl * row_x + c8 * 16) : kOffMasked;
     const uint32_t lane_f = tok_ok ? (uint32_t)(tl * row_f + c8 * 16) : kOffMasked;
-    const uint32_t lane_p = (uint32_t)(lane * 16);
+    // MFMA role, B operand lane (k-group g = lane/16, column col = lane%16): fp32
+    // weights of mix row col (column tile 0) and 16 + col%8 (tile 1), channels
+    // 8g .. 8g+7 of stream mj's k-block
+    const int g = lane >> 4, col = lane & 15;
+    const uint32_t lane_w0 = (uint32_t)(((int64_t)col * kHC * d + (int64_t)mj * d + g * 8) * 4);
+    const uint32_t lane_w1 = (uint32_t)(((int64_t)(16 + (col & 7)) * kHC * d + (int64_t)mj * d + g * 8) * 4);
 
     auto load_step = [&](StepRegs<kPost>& R, int s) {
         const int64_t cs = c_begin + (int64_t)s * kStep;
@@ -860,22 +832,25 @@ __global__ __launch_bounds__(kSwBlock) void bf16_sweep_kernel(PassArgs a, const 
         for (int j = 0; j < kHC; ++j) R.x[j] = buf_load16(rx, vx, so + (uint32_t)(j * row_f));
         if constexpr (kPost) R.f = buf_load16(rf, vf, so);
     };
-    // the 5 B operands of (stream mj, k-block mkk of step s); past the slice: zeros
-    auto load_b = [&](uint4 (&B)[kFragsPerKb], int s) {
+    // fp32 weights of (stream mj, k-block mkk of step s): 8 channels of two mix
+    // rows per lane; past the slice or past d: zeros
+    auto load_b = [&](float4 (&W)[4], int s) {
         const int kb = kb_begin + s * kStepKb + mkk;
-        const uint32_t v = kb < kb_end ? lane_p : kOffMasked;
-#pragma unroll
-        for (int q = 0; q < kFragsPerKb; ++q)
-            B[q] = buf_load16(rp, v, (uint32_t)((((int64_t)mj * nkb + kb) * kFragsPerKb + q) * 64 * 16));
+        const bool ok = kb < kb_end && (int64_t)kb * kChunk + g * 8 < d;   // d % 8 == 0: whole groups
+        const uint32_t v0 = ok ? lane_w0 : kOffMasked, v1 = ok ? lane_w1 : kOffMasked;
+        const uint32_t so = (uint32_t)(kb * kChunk * 4);
+        W[0] = buf_load16f(rw, v0, so);
+        W[1] = buf_load16f(rw, v0 + 16u, so);
+        W[2] = buf_load16f(rw, v1, so);
+        W[3] = buf_load16f(rw, v1 + 16u, so);
     };
 
     floatx4_t acc[4][2], gram[4];
 #pragma unroll
     for (int T = 0; T < 4; ++T) acc[T][0] = acc[T][1] = gram[T] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto step = [&](int s, StepRegs<kPost>& cur, StepRegs<kPost>& ahead, uint4 (&Bcur)[kFragsPerKb],
-                    uint4 (&Bnext)[kFragsPerKb]) {
-        load_b(Bnext, s + 1);
+    auto step = [&](int s, StepRegs<kPost>& cur, StepRegs<kPost>& ahead, float4 (&Wcur)[4], float4 (&Wnext)[4]) {
+        load_b(Wnext, s + 1);
         load_step(ahead, s + 2);
         const int64_t cs = c_begin + (int64_t)s * kStep;
         const bool ok = cs + c8 * 8 < c_end;
@@ -923,6 +898,15 @@ __global__ __launch_bounds__(kSwBlock) void bf16_sweep_kernel(PassArgs a, const 
 #pragma unroll
         for (int j = 0; j < kHC; ++j) A[a_slot(tl, j, c8)] = cur.x[j];
         __syncthreads();   // A buffer complete; the other buffer is free again
+        // B operands: weights split into three bf16 terms (hi + mid + lo); column
+        // tile 1 packs [hi | mid] and [lo | 0] of mixes 16..23 into two operands
+        uint4 Bcur[kFragsPerKb], hi1, mid1, lo1;
+        split3(Wcur[0], Wcur[1], Bcur[0], Bcur[1], Bcur[2]);
+        split3(Wcur[2], Wcur[3], hi1, mid1, lo1);
+        const bool lo_half = col < 8;
+        Bcur[3] = make_uint4(lo_half ? hi1.x : mid1.x, lo_half ? hi1.y : mid1.y, lo_half ? hi1.z : mid1.z,
+                             lo_half ? hi1.w : mid1.w);
+        Bcur[4] = make_uint4(lo_half ? lo1.x : 0u, lo_half ? lo1.y : 0u, lo_half ? lo1.z : 0u, lo_half ? lo1.w : 0u);
 #pragma unroll
         for (int T = 0; T < 4; ++T) {
             const bf16x8_t Av =
@@ -936,33 +920,33 @@ __global__ __launch_bounds__(kSwBlock) void bf16_sweep_kernel(PassArgs a, const 
     };
 
     StepRegs<kPost> R0, R1, R2;
-    uint4 B0[kFragsPerKb], B1[kFragsPerKb];
+    float4 B0[4], B1[4];
     load_b(B0, 0);
     load_step(R0, 0);
     load_step(R1, 1);
-    // every exit leaves the loop: the back edge is only reached after all six
-    // steps, so the loads pending at the loop head are always the same sets
-    for (int s = 0;; s += 6) {
+    // Whole groups of six steps in a loop without exits, the remaining steps
+    // after it: the loads pending at the loop head are then the same on every
+    // path into it, and the compiler need not drain them there.
+    int s = 0;
+    for (; s + 6 <= nst; s += 6) {
         step(s, R0, R2, B0, B1);
-        if (s + 1 >= nst) break;
         step(s + 1, R1, R0, B1, B0);
-        if (s + 2 >= nst) break;
         step(s + 2, R2, R1, B0, B1);
-        if (s + 3 >= nst) break;
         step(s + 3, R0, R2, B1, B0);
-        if (s + 4 >= nst) break;
         step(s + 4, R1, R0, B0, B1);
-        if (s + 5 >= nst) break;
         step(s + 5, R2, R1, B1, B0);
-        if (s + 6 >= nst) break;
     }
+    if (s < nst) step(s, R0, R2, B0, B1);
+    if (s + 1 < nst) step(s + 1, R1, R0, B1, B0);
+    if (s + 2 < nst) step(s + 2, R2, R1, B0, B1);
+    if (s + 3 < nst) step(s + 3, R0, R2, B1, B0);
+    if (s + 4 < nst) step(s + 4, R1, R0, B0, B1);
 
     __syncthreads();   // every wave is done with the A buffers
 #pragma unroll
     for (int T = 0; T < 4; ++T)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) acc[T][1][ii] += dpp<kRowRor8>(acc[T][1][ii]);
-    const int g = lane >> 4, col = lane & 15;
     float* red = reinterpret_cast<float*>(&lds.a[0][0]);   // [wave][T][nt][ii][lane], 64 KB
 #pragma unroll
     for (int T = 0; T < 4; ++T)
@@ -1023,10 +1007,8 @@ PassPlan plan_pass(int64_t n, int64_t d, bool bf16) {
     if (ns > 64) ns = 64;
     p.chunks_per_split = (int)ceil_div(nunits, ns) * (unit / kChunk);
     p.nsplit = (int)ceil_div(p.nchunks, p.chunks_per_split);
-    // [partial rows: nsplit x n x 32 floats][packed weights: 4 streams x nchunks x 5 x 1 KB]
-    p.partial_bytes = (size_t)p.nsplit * (size_t)n * kPart * sizeof(float);
-    p.packed_bytes = (size_t)kHC * (size_t)p.nchunks * kFragsPerKb * 64 * 16;
-    p.workspace_bytes = p.partial_bytes + p.packed_bytes;
+    // partial rows: nsplit x n x 32 floats
+    p.workspace_bytes = (size_t)p.nsplit * (size_t)n * kPart * sizeof(float);
     return p;
 }
 
@@ -1064,9 +1046,9 @@ hipError_t launch_post(const void* f, const void* res, bool bf16, const float* p
 
 namespace {
 template <bool kPost, bool kPre>
-void launch_sweep_t(const PassArgs& a, const PassPlan& p, const uint4* packed, hipStream_t stream) {
+void launch_sweep_t(const PassArgs& a, const PassPlan& p, hipStream_t stream) {
     hipLaunchKernelGGL((bf16_sweep_kernel<kPost, kPre>), dim3((unsigned)(p.tiles * p.nsplit)), dim3(kSwBlock), 0,
-                       stream, a, packed);
+                       stream, a);
 }
 
 template <bool kPost, bool kPre>
@@ -1110,14 +1092,10 @@ hipError_t launch_pass_and_finalize(const PassRequest& r, hipStream_t stream) {
     f.comb = r.comb;
     const bool post = r.f_prev != nullptr, pre = r.y != nullptr;
     if (r.bf16) {
-        // weights split into bf16 terms in MFMA B layout, once per call
-        uint4* packed = reinterpret_cast<uint4*>(static_cast<char*>(r.workspace) + p.partial_bytes);
-        hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)ceil_div((int64_t)kHC * p.nchunks * 64, 256)),
-                           dim3(256), 0, stream, r.hc_fn, r.d, p.nchunks, packed);
-        if (post && pre) launch_sweep_t<true, true>(a, p, packed, stream);
-        else if (post) launch_sweep_t<true, false>(a, p, packed, stream);
-        else if (pre) launch_sweep_t<false, true>(a, p, packed, stream);
-        else launch_sweep_t<false, false>(a, p, packed, stream);
+        if (post && pre) launch_sweep_t<true, true>(a, p, stream);
+        else if (post) launch_sweep_t<true, false>(a, p, stream);
+        else if (pre) launch_sweep_t<false, true>(a, p, stream);
+        else launch_sweep_t<false, false>(a, p, stream);
     } else {
         if (post && pre) launch_pass_t<true, true>(a, p, stream);
         else if (post) launch_pass_t<true, false>(a, p, stream);

@@ -56,17 +56,15 @@ def test_version_and_status_strings():
 
 
 def test_workspace_size_rule():
-    # [one 128-byte partial row per (channel slice, token); slices are whole
-    #  64- or 128-channel steps][the weights split into bf16 terms: 4 streams x
-    #  ceil(d/32) k-blocks x 5 B operands x 1 KB]
+    # one 128-byte partial row per (channel slice, token); slices are whole 64-
+    # (bf16) or 128-channel (fp32) steps, at most 64 of them
     assert hc.workspace_size(0, 4, 5120) == 0
     assert hc.workspace_size(16, 3, 5120) == 0
     assert hc.workspace_size(16, 4, 12) == 0
     for n, d in ((16, 256), (64, 5120), (4096, 5120), (65536, 5120), (37, 264)):
         ws = hc.workspace_size(n, 4, d)
-        part = ws - 4 * (-(-d // 32)) * 5 * 1024
-        assert part > 0 and part % (128 * n) == 0
-        nsplit = part // (128 * n)
+        assert ws > 0 and ws % (128 * n) == 0
+        nsplit = ws // (128 * n)
         assert 1 <= nsplit <= min(64, -(-d // 64))
 
 
