@@ -28,8 +28,8 @@ KERNEL_SOURCES = ("hyper_connection_residual_mixes_amd/csrc/hc_kernels.hip",
                   "hyper_connection_residual_mixes_amd/csrc/hc_internal.h")
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "ffn_boundary_counters_prefill_T4096.md")
 ENTRY_KERNELS = {
-    "attn_fused": "pack_weights_kernel + bf16_sweep_kernel<no expand, collapse> + finalize_kernel",
-    "ffn_fused": "pack_weights_kernel + bf16_sweep_kernel<expand, collapse> + finalize_kernel",
+    "attn_fused": "bf16_sweep_kernel<no expand, collapse> + finalize_kernel",
+    "ffn_fused": "bf16_sweep_kernel<expand, collapse> + finalize_kernel",
     "ffn_post": "post_kernel",
 }
 
