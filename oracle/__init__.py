@@ -67,6 +67,8 @@ def _load():
     lib.oracle_hc_pre.argtypes = [P, I, P, I64, I, I64, P]
     lib.oracle_hc_post.argtypes = [P, P, I, P, P, I64, I, I64, P]
     lib.oracle_round_bf16.argtypes = [D]
+    lib.oracle_rmsnorm.argtypes = [P, I, I64, I64, P, D, P]
+    lib.oracle_mxfp8.argtypes = [P, I, I64, I64, P, P]
     lib.oracle_round_bf16.restype = ctypes.c_uint16
     for name in ("oracle_hc_mixes", "oracle_hc_split_sinkhorn", "oracle_hc_pre", "oracle_hc_post"):
         getattr(lib, name).restype = I
@@ -218,6 +220,30 @@ def block(x, pre_mix, attn, ffn, f_attn, f_ffn, sinkhorn_iters=SINKHORN_ITERS, e
     x2 = hc_post(f_ffn, x1, postF, combF)
     return dict(yA=yA, mixesA=mA, preA=preA, postA=postA, combA=combA, x1=x1,
                 yF=yF, mixesF=mF, preF=preF, postF=postF, combF=combF, x2=x2)
+
+
+def rmsnorm(x: torch.Tensor, gain: torch.Tensor, norm_eps: float = NORM_EPS) -> torch.Tensor:
+    """RMSNorm of the collapsed input over its last (channel) axis, with a learned
+    per-channel gain; result in the dtype of x. x: [..., d], gain: [d] fp32."""
+    d = x.shape[-1]
+    xc = _cpu(x)
+    g = _cpu(gain, torch.float32)
+    out = torch.empty_like(xc)
+    n = xc.numel() // d
+    _check(_load().oracle_rmsnorm(_ptr(xc), _dtype_code(xc), n, d, _ptr(g), norm_eps, _ptr(out)), "rmsnorm")
+    return out
+
+
+def mxfp8(x: torch.Tensor):
+    """MXFP8 cast over the last axis (groups of 32 channels): returns (codes uint8
+    [..., d] in E4M3, scales uint8 [..., d/32] in UE8M0)."""
+    d = x.shape[-1]
+    xc = _cpu(x)
+    n = xc.numel() // d
+    q = torch.empty(xc.shape, dtype=torch.uint8)
+    sc = torch.empty(*xc.shape[:-1], d // 32, dtype=torch.uint8)
+    _check(_load().oracle_mxfp8(_ptr(xc), _dtype_code(xc), n, d, _ptr(q), _ptr(sc)), "mxfp8")
+    return q, sc
 
 
 def param_shapes(hc: int, d: int):

@@ -15,7 +15,12 @@
  *               kernel and its wrapper), released configuration.
  *   [Diagram]   "DeepSeek-V4.1-Flash" diagram page: blocks "Mixing
  *               Coefficients", "sigma", "x + eps_hc", "2 sigma",
- *               "First Sinkhorn Round", "Sinkhorn Round", "Cast".
+ *               "First Sinkhorn Round", "Sinkhorn Round", "Cast",
+ *               "Single-Pass mHC" (the hidden state is normalised after the
+ *               collapse), "Cast to MXFP8".
+ *   [Donor]     "DeepSeek-R1 donor reference" page: the RMSNorm passages
+ *               ("Normalize by the root mean square", "Apply learned
+ *               per-feature RMSNorm gains").
  *
  * Arithmetic: every sum and product is carried out in double precision
  * (fp64). A value is rounded exactly once, to the precision of the tensor the
@@ -286,5 +291,104 @@ int oracle_hc_post(const void* f, const void* residual, int dtype, const float* 
                            load_elem(residual, dtype, (t * hc + j) * d + e);
                 store_elem(out, dtype, (t * hc + k) * d + e, acc);
             }
+    return 0;
+}
+
+
+/*
+ * Sublayer RMSNorm after the collapse ([Block] Block.forward applies attn_norm /
+ * ffn_norm, RMSNorm(dim, norm_eps), to the collapsed input; [Donor] RMSNorm
+ * passages; [Diagram] "Single-Pass mHC").
+ * out[t][e] = x[t][e] / sqrt(mean_e x[t][e]^2 + eps) * gain[e], over the d
+ * channels of the row, rounded once to the dtype of x (the gain multiplies the
+ * scaled value, then the earlier dtype is restored).
+ */
+int oracle_rmsnorm(const void* x, int dtype, int64_t n, int64_t d, const float* gain, double eps,
+                   void* out)
+{
+    if (n < 0 || d < 1 || bad_dtype(dtype) || !(eps >= 0.0))
+        return -1;
+    if (n == 0)
+        return 0;
+    if (!x || !gain || !out)
+        return -1;
+    for (int64_t t = 0; t < n; ++t) {
+        double ss = 0.0;
+        for (int64_t e = 0; e < d; ++e) {
+            const double v = load_elem(x, dtype, t * d + e);
+            ss += v * v;
+        }
+        const double r = 1.0 / sqrt(ss / (double)d + eps);
+        for (int64_t e = 0; e < d; ++e)
+            store_elem(out, dtype, t * d + e, load_elem(x, dtype, t * d + e) * r * (double)gain[e]);
+    }
+    return 0;
+}
+
+/* E4M3 (4 exponent bits, bias 7, 3 mantissa bits; largest finite 448, smallest
+ * subnormal 2^-9) of a value with |v| <= 448, rounded to the nearest code, ties
+ * to the even code; the sign is kept (a value that rounds to zero keeps it). */
+static uint8_t e4m3_code(double v)
+{
+    const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    const double a = fabs(v);
+    if (a < ldexp(1.0, -6)) {                     /* subnormal codes: multiples of 2^-9 */
+        const double q = nearbyint(ldexp(a, 9));   /* 0..8; 8 is the smallest normal */
+        return sign | (uint8_t)q;
+    }
+    int e;
+    const double m = frexp(a, &e);                 /* a = m * 2^e, m in [0.5, 1) */
+    int exp = e - 1;                               /* a = (2m) * 2^exp, 2m in [1, 2) */
+    double mant = nearbyint((2.0 * m - 1.0) * 8.0);   /* 3 fraction bits, ties to even */
+    if (mant == 8.0) {
+        mant = 0.0;
+        exp += 1;
+    }
+    return sign | (uint8_t)(((exp + 7) << 3) | (int)mant);
+}
+
+/* ceil(log2(v)) for v > 0, exactly (frexp: v = m * 2^e, m in [0.5, 1)). */
+static int ceil_log2(double v)
+{
+    int e;
+    const double m = frexp(v, &e);
+    return m == 0.5 ? e - 1 : e;
+}
+
+/*
+ * MXFP8 cast ([Diagram] "Cast to MXFP8"): the channels of a row are cut into
+ * groups of 32. Group g: a = max |x| over the group; its scale is the power of two
+ * s = 2^ceil(log2(max(a, 1e-4) / 448)), stored as the UE8M0 byte log2(s) + 127;
+ * each element is x / s, clamped to [-448, 448] and rounded to the nearest E4M3
+ * code. d must be a multiple of 32. x / s is exact (s is a power of two), and
+ * since s >= a / 448 the clamp never acts; it is kept as the page states it.
+ */
+int oracle_mxfp8(const void* x, int dtype, int64_t n, int64_t d, uint8_t* q, uint8_t* scale)
+{
+    if (n < 0 || d < 32 || d % 32 != 0 || bad_dtype(dtype))
+        return -1;
+    if (n == 0)
+        return 0;
+    if (!x || !q || !scale)
+        return -1;
+    for (int64_t t = 0; t < n; ++t)
+        for (int64_t g = 0; g < d / 32; ++g) {
+            double a = 0.0;
+            for (int i = 0; i < 32; ++i) {
+                const double v = fabs(load_elem(x, dtype, t * d + g * 32 + i));
+                if (v > a)
+                    a = v;
+            }
+            const int k = ceil_log2((a > 1e-4 ? a : 1e-4) / 448.0);
+            scale[t * (d / 32) + g] = (uint8_t)(k + 127);
+            for (int i = 0; i < 32; ++i) {
+                double v = ldexp(load_elem(x, dtype, t * d + g * 32 + i), -k);
+                if (v > 448.0)
+                    v = 448.0;
+                if (v < -448.0)
+                    v = -448.0;
+                q[t * d + g * 32 + i] = e4m3_code(v);
+            }
+        }
     return 0;
 }

@@ -39,6 +39,16 @@ MUTANTS = {
                                            "(double)comb[(t * hc + k) * hc + j]"),
     "post drops f": ("(double)post[t * hc + k] * load_elem(f, dtype, t * d + e)", "0.0"),
     "bf16 truncation instead of rounding": ("nearbyint(ldexp(m, 8))", "floor(ldexp(m, 8))"),
+    "rmsnorm mean over d - 1": ("sqrt(ss / (double)d + eps)", "sqrt(ss / (double)(d - 1) + eps)"),
+    "rmsnorm gain dropped": ("* r * (double)gain[e]", "* r"),
+    "rmsnorm eps replaced": ("sqrt(ss / (double)d + eps)", "sqrt(ss / (double)d + 1e-6)"),
+    "mxfp8 no 1e-4 floor": ("(a > 1e-4 ? a : 1e-4)", "(a > 0.0 ? a : 1e-30)"),
+    "mxfp8 scale rounded down": ("return m == 0.5 ? e - 1 : e;", "return e - 1;"),
+    "mxfp8 divide by 256": ("/ 448.0);", "/ 256.0);"),
+    "e4m3 mantissa truncated": ("nearbyint((2.0 * m - 1.0) * 8.0)", "floor((2.0 * m - 1.0) * 8.0)"),
+    "e4m3 subnormal step 2^-10": ("nearbyint(ldexp(a, 9))", "nearbyint(ldexp(a, 10))"),
+    "e4m3 sign dropped": ("signbit(v) ? 0x80 : 0x00", "0x00"),
+    "e4m3 exponent bias 8": ("(((exp + 7) << 3)", "(((exp + 8) << 3)"),
 }
 
 

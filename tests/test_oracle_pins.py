@@ -372,3 +372,101 @@ def test_block_wiring_collapse_uses_previous_sublayer_pre():
             assert torch.equal(a[k], b[k]), k
     assert torch.equal(a["yF"], oracle.hc_pre(a["x1"], a["preA"]))
     assert not torch.equal(a["yF"], oracle.hc_pre(a["x1"], a["preF"]))
+
+
+# ------------------------------------------------ RMSNorm and MXFP8 cast (next rows)
+def _group_with_unit_scale(vals):
+    """Groups of 32 whose first element is 448, so the group scale is 2^0 and the
+    codes of the other 31 elements are the plain E4M3 codes of their values."""
+    vals = list(vals)
+    rows = []
+    for i in range(0, len(vals), 31):
+        chunk = vals[i:i + 31]
+        chunk += [0.0] * (31 - len(chunk))
+        rows.append([448.0] + chunk)
+    return torch.tensor(rows, dtype=torch.float32)
+
+
+def test_e4m3_codes_match_torch_float8():
+    """E4M3 rounding ([Diagram] "Cast to MXFP8": nearest E4M3 number) against
+    torch's independent float8_e4m3fn conversion: random values over the whole
+    range, the subnormal range, and exact midpoints between neighbouring codes."""
+    g = hc_inputs.generator(3)
+    vals = (torch.rand(3000, generator=g) * 2 - 1) * 448
+    vals = torch.cat([vals, (torch.rand(1000, generator=g) * 2 - 1) * 2.0 ** -6])
+    mids = []
+    for e in range(-6, 8):
+        for m in range(8):
+            mids.append((1 + (m + 0.5) / 8) * 2.0 ** e)   # halfway between two codes
+    for m in range(8):
+        mids.append((m + 0.5) * 2.0 ** -9)                 # subnormal midpoints
+    vals = torch.cat([vals, torch.tensor(mids), -torch.tensor(mids)])
+    x = _group_with_unit_scale(vals.tolist())
+    q, sc = oracle.mxfp8(x)
+    assert (sc == 127).all()
+    ref = x[:, 1:].to(torch.float8_e4m3fn).view(torch.uint8)
+    assert torch.equal(q[:, 1:], ref)
+    assert (q[:, 0] == 0x7E).all()                         # 448 is the largest finite code
+
+
+def test_mxfp8_page_extremes_and_sign():
+    """The page's statements: E4M3 tops out at 448 and flushes below 2^-9 without a
+    scale; a value halfway to the smallest subnormal rounds to the even code 0;
+    the sign of a value that rounds to zero is kept."""
+    x = _group_with_unit_scale([2.0 ** -9, 2.0 ** -10, 1.5 * 2.0 ** -10, -2.0 ** -12, 447.0, -448.0])
+    q, _ = oracle.mxfp8(x)
+    assert q[0, 1:7].tolist() == [0x01, 0x00, 0x01, 0x80, 0x7E, 0xFE]
+
+
+def test_mxfp8_group_scales_hand_cases():
+    """UE8M0 scale = 2^ceil(log2(max(amax, 1e-4) / 448)), byte = exponent + 127."""
+    cases = {   # amax -> exponent of the scale
+        448.0: 0, 450.0: 1, 224.0: -1, 225.0: 0, 896.0: 1, 897.0: 2, 1.0: -8,
+        1e-4: -22, 1e-6: -22, 0.0: -22, 3.5: -7, 3.0 * 2 ** 100: 93,   # 100 + log2(3/448) = 92.8
+    }
+    rows = [[a] + [0.0] * 31 for a in cases]
+    q, sc = oracle.mxfp8(torch.tensor(rows, dtype=torch.float32))
+    assert sc[:, 0].tolist() == [k + 127 for k in cases.values()]
+    # 450 / 2 = 225 = 1.7578 * 2^7 -> mantissa 6.06 -> 6: code (7 + 7) << 3 | 6
+    assert q[1, 0].item() == 0x76
+    # a group whose amax is exactly 448 * 2^k is scaled to exactly 448
+    q2, sc2 = oracle.mxfp8(torch.tensor([[448.0 * 8] + [-3.0] * 31], dtype=torch.float32))
+    assert sc2.item() == 130 and q2[0, 0].item() == 0x7E
+    # dequantised values stay within half an E4M3 step of the scaled input
+    g = hc_inputs.generator(4)
+    x = torch.randn(64, 256, generator=g) * torch.logspace(-6, 6, 64).unsqueeze(1)
+    q3, sc3 = oracle.mxfp8(x)
+    deq = q3.view(torch.float8_e4m3fn).float() * torch.pow(2.0, sc3.float() - 127).repeat_interleave(32, 1)
+    s = torch.pow(2.0, sc3.float() - 127).repeat_interleave(32, 1)
+    step = torch.where(x.abs() / s < 2 ** -6, torch.full_like(x, 2.0 ** -9), 2.0 ** (torch.floor(torch.log2((x.abs() / s).clamp_min(2 ** -6))) - 3))
+    assert ((deq - x).abs() <= step * s / 2 * (1 + 1e-6)).all()
+
+
+def test_rmsnorm_closed_forms():
+    """RMSNorm ([Donor] RMSNorm passages; [Block] RMSNorm(dim, norm_eps)): a constant
+    row maps to the gain (times its sign); (3, 4, 0, 0) has RMS 2.5 and maps to
+    (1.2, 1.6, 0, 0) x gain; scaling a row by a power of two changes nothing; the
+    epsilon keeps an all-zero row at zero."""
+    gain = torch.tensor([0.5, 2.0, -1.0, 3.0])
+    x = torch.tensor([[7.0, 7.0, 7.0, 7.0], [-0.25, -0.25, -0.25, -0.25], [3.0, 4.0, 0.0, 0.0],
+                      [0.0, 0.0, 0.0, 0.0]])
+    out = oracle.rmsnorm(x, gain)
+    assert torch.allclose(out[0], gain, rtol=1e-7, atol=0)
+    assert torch.allclose(out[1], -gain, rtol=1e-7, atol=0)
+    assert torch.allclose(out[2], torch.tensor([0.6, 3.2, 0.0, 0.0]), rtol=1e-6, atol=0)
+    assert torch.equal(out[3], torch.zeros(4))
+    g = hc_inputs.generator(5)
+    xr = torch.randn(8, 512, generator=g).to(torch.bfloat16)
+    gr = torch.rand(512, generator=g) + 0.5
+    assert torch.equal(oracle.rmsnorm(xr, gr), oracle.rmsnorm(xr * 8, gr))
+    assert oracle.rmsnorm(xr, gr).dtype == torch.bfloat16
+
+
+def test_rmsnorm_uses_norm_eps():
+    """With eps = norm_eps = 1e-20 a tiny constant row still normalises to the gain;
+    with a large eps the output shrinks by sqrt(ms / (ms + eps))."""
+    x = torch.full((1, 64), 1e-6)
+    gain = torch.ones(64)
+    assert torch.allclose(oracle.rmsnorm(x, gain), torch.ones(1, 64), rtol=1e-6, atol=0)
+    out = oracle.rmsnorm(torch.full((1, 64), 2.0), gain, norm_eps=12.0)   # 2 / sqrt(4 + 12)
+    assert torch.allclose(out, torch.full((1, 64), 0.5), rtol=1e-7, atol=0)
