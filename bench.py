@@ -185,6 +185,26 @@ def main():
         copy_gbs = 2 * src.numel() * 2 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
         del src, dst
 
+    # next row: RMSNorm + MXFP8 cast of the attention boundary's collapsed input
+    # (cast only, the GEMM-ready operand), timed with HIP events on its own
+    gain = torch.rand(d, generator=torch.Generator(device=dev).manual_seed(5), device=dev) + 0.5
+    qbuf = torch.empty(n, d, dtype=torch.uint8, device=dev)
+    sbuf = torch.empty(n, d // 32, dtype=torch.uint8, device=dev)
+    for i in range(3):
+        hc.rmsnorm_mxfp8(sets[i % len(sets)][2]["yA"], gain, want_norm=False, q=qbuf, scale=sbuf)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        hc.rmsnorm_mxfp8(sets[i % len(sets)][2]["yA"], gain, want_norm=False, q=qbuf, scale=sbuf)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    norm_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    norm_bytes = n * (2 * d + d + d // 32) + 4 * d     # y in, codes + scales out, gain once
+    next_rows = {"rmsnorm_mxfp8": {
+        "workload": f"RMSNorm (gain) + MXFP8 cast of the collapsed input, {n} x {d} bf16 -> E4M3 + UE8M0",
+        "kernel": "rmsnorm_mxfp8_kernel", "us": norm_us, "algorithmic_bytes": norm_bytes,
+        "achieved_gb_s": norm_bytes / norm_us / 1e3, "frac": norm_bytes / norm_us / 1e3 / PEAK_HBM_GBS}}
+
     result = {
         "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
@@ -203,6 +223,7 @@ def main():
                                      "frac": ab[k] / per[k] / 1e9 / PEAK_HBM_GBS,
                                      "traffic": stored_traffic(k)} for k in per},
     }
+    result["next_rows"] = next_rows
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on every input set", file=sys.stderr, flush=True)
         cpu = lambda t: t.cpu() if isinstance(t, torch.Tensor) else tuple(u.cpu() for u in t)

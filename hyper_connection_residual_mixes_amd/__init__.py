@@ -51,9 +51,10 @@ def lib():
     L.hc_split_sinkhorn.argtypes = [P, P, P, I64, I, I, F, P, P, P, P]
     L.hc_pre.argtypes = [P, I, P, I64, I, I64, P, P]
     L.hc_post.argtypes = [P, P, I, P, P, I64, I, I64, P, P]
+    L.hc_rmsnorm_mxfp8.argtypes = [P, I, P, I64, I64, F, P, P, P, P]
     L.hc_fused_step.argtypes = [P, P, P, P, P, P, P, P, I64, I, I64, I, F, I, F,
                                 P, P, P, P, P, P, P, SZ, P]
-    for name in ("hc_mixes", "hc_split_sinkhorn", "hc_pre", "hc_post", "hc_fused_step"):
+    for name in ("hc_mixes", "hc_split_sinkhorn", "hc_pre", "hc_post", "hc_fused_step", "hc_rmsnorm_mxfp8"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -178,6 +179,31 @@ def hc_post(f, residual, post, comb, out=None):
     _check("hc_post", lib().hc_post(_ptr(f), _ptr(residual), _dtype_code(f), _ptr(post), _ptr(comb), n,
                                     hc, d, _ptr(out), _stream(f.device)))
     return out
+
+
+def rmsnorm_mxfp8(x, gain, norm_eps=NORM_EPS, want_norm=True, want_cast=True, y_norm=None, q=None,
+                  scale=None):
+    """The sublayer RMSNorm (learned gain) of a collapsed input x [..., d] and its
+    MXFP8 cast (groups of 32 channels). Returns dict(y_norm, q, scale): y_norm in
+    x's dtype, q E4M3 codes uint8 [..., d], scale UE8M0 bytes uint8 [..., d/32];
+    entries not requested are None."""
+    _dev(x, "x")
+    _dev(gain, "gain", torch.float32)
+    d = x.shape[-1]
+    n = x.numel() // d if d else 0
+    if want_norm and y_norm is None:
+        y_norm = torch.empty_like(x)
+    if want_cast:
+        if q is None:
+            q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+        if scale is None:
+            scale = torch.empty(*x.shape[:-1], d // 32, dtype=torch.uint8, device=x.device)
+    else:
+        q = scale = None
+    _check("hc_rmsnorm_mxfp8", lib().hc_rmsnorm_mxfp8(
+        _ptr(x), _dtype_code(x), _ptr(gain), n, d, float(norm_eps), _ptr(y_norm) if want_norm else None,
+        _ptr(q), _ptr(scale), _stream(x.device)))
+    return dict(y_norm=y_norm if want_norm else None, q=q, scale=scale)
 
 
 def hc_fused_step(residual, hc_fn, hc_scale, hc_base, pre_mix=None, f_prev=None, post_prev=None,

@@ -122,6 +122,31 @@ int hc_pre(const void* x, int dtype, const float* pre_mix, int64_t n, int hc, in
     return hip_status(hc::launch_pre(x, dtype == HC_BF16, pre_mix, n, d, y, static_cast<hipStream_t>(stream)));
 }
 
+int hc_rmsnorm_mxfp8(const void* x, int dtype, const float* gain, int64_t n, int64_t d, float norm_eps,
+                     void* y_norm, uint8_t* q, uint8_t* scale, void* stream) {
+    if (n < 0 || d < 8 || d > (int64_t(1) << 20)) return HC_ERR_SHAPE;
+    if (n > 0 && (uint64_t)d > (uint64_t(1) << 40) / (uint64_t)n) return HC_ERR_SHAPE;
+    if (n > 0x7fffffff) return HC_ERR_SHAPE;                     // one workgroup per row
+    if (dtype != HC_F32 && dtype != HC_BF16) return HC_ERR_UNSUPPORTED;
+    if (d % 8 != 0) return HC_ERR_UNSUPPORTED;
+    if (check_eps(norm_eps) != HC_OK) return HC_ERR_ARG;
+    if ((q == nullptr) != (scale == nullptr)) return HC_ERR_NULL;  // codes and scales come together
+    if (q && d % 32 != 0) return HC_ERR_UNSUPPORTED;
+    if (!y_norm && !q) return HC_ERR_ARG;                          // nothing to produce
+    if (n == 0) return HC_OK;
+    if (!x || !gain) return HC_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(gain, 16) || (y_norm && !aligned(y_norm, 16)) || (q && !aligned(q, 8)))
+        return HC_ERR_ALIGN;
+    const size_t es = elem_size(dtype), un = (size_t)n, ud = (size_t)d;
+    const Span x_span{x, un * ud * es};
+    const Span outs[] = {{y_norm, un * ud * es}, {q, q ? un * ud : 0}, {scale, scale ? un * (ud / 32) : 0}};
+    const Span ins[] = {x_span, {gain, ud * 4}};
+    const Span allowed[] = {{y_norm, un * ud * es}, x_span};         // in place: y_norm == x
+    if (int rc = check_aliases(outs, 3, ins, 2, allowed, 1)) return rc;
+    return hip_status(hc::launch_rmsnorm_mxfp8(x, dtype == HC_BF16, gain, n, d, norm_eps, y_norm, q, scale,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 int hc_post(const void* f, const void* residual, int dtype, const float* post, const float* comb, int64_t n,
             int hc, int64_t d, void* out, void* stream) {
     if (int rc = check_shape(n, hc, d, dtype)) return rc;

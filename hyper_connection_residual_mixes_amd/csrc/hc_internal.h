@@ -54,5 +54,7 @@ hipError_t launch_pre(const void* x, bool bf16, const float* pre_mix, int64_t n,
 hipError_t launch_post(const void* f, const void* res, bool bf16, const float* post, const float* comb,
                        int64_t n, int64_t d, void* out, hipStream_t stream);
 hipError_t launch_pass_and_finalize(const PassRequest& r, hipStream_t stream);
+hipError_t launch_rmsnorm_mxfp8(const void* x, bool bf16, const float* gain, int64_t n, int64_t d, float eps,
+                                void* y_norm, uint8_t* q, uint8_t* scale, hipStream_t stream);
 
 }  // namespace hc

@@ -18,6 +18,8 @@
 //   pass_kernel         the same pass for fp32 streams (fp32 MFMA).
 //   finalize_kernel     16 lanes per token: reduce the slice partials in a fixed
 //                       order, scale by the RMS statistic, and (optionally) split.
+//   rmsnorm_mxfp8_kernel the sublayer RMSNorm (learned gain) of the collapsed
+//                       input and its MXFP8 cast, one workgroup per token row.
 //
 // All arithmetic is fp32 (MFMA products exact, fp32 accumulation). bf16 values
 // are rounded to nearest-even (v_cvt_pk_bf16_f32).
@@ -984,6 +986,110 @@ __global__ __launch_bounds__(kSwBlock) void bf16_sweep_kernel(PassArgs a) {
     }
 }
 
+// ------------------------------------------- sublayer RMSNorm + MXFP8 cast
+// The sublayer input after the collapse is RMS-normalised with a learned gain
+// (Block.forward: attn_norm / ffn_norm) and cast to MXFP8 for the projections
+// that read it (diagram "Cast to MXFP8"). One workgroup per token row: pass 1
+// sums the squares of the row; pass 2 re-reads it (L1/L2 hit), multiplies by
+// 1/sqrt(mean + eps) and the gain, rounds to the row dtype (the normalised
+// output), and casts groups of 32 channels: four consecutive lanes own a group
+// (8 channels each), its amax is combined with two quad DPP steps.
+constexpr int kNormBlock = 256;
+
+// ceil(log2(max(a, 1e-4) / 448)) for a >= 0, exactly: 448 = 1.75 * 2^8, so for
+// a = m * 2^e (m in [1, 2)) the exponent is e - 8, plus one when m > 1.75.
+__device__ __forceinline__ int mx_scale_exp(float a) {
+    const uint32_t b = __float_as_uint(fmaxf(a, 1e-4f));
+    const int e = (int)(b >> 23) - 127;
+    return e - 8 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0);
+}
+
+// E4M3 code of v (|v| <= 448): nearest code, ties to the even code, sign kept.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+    const uint32_t bits = __float_as_uint(v);
+    const uint32_t sign = (bits >> 24) & 0x80u;
+    const float a = fabsf(v);
+    if (a < 0.015625f)   // below 2^-6: subnormal codes, multiples of 2^-9 (code 8 = 2^-6)
+        return sign | (uint32_t)__builtin_rintf(a * 512.0f);
+    const uint32_t ab = __float_as_uint(a);
+    uint32_t exp = (ab >> 23) - 127 + 7;            // biased E4M3 exponent, 1..15
+    uint32_t mant = (ab >> 20) & 7u;
+    const uint32_t rest = ab & 0xfffffu, half = 0x80000u;
+    if (rest > half || (rest == half && (mant & 1u))) ++mant;
+    if (mant == 8u) {
+        mant = 0;
+        ++exp;
+    }
+    return sign | (exp << 3) | mant;
+}
+
+template <bool kBf16>
+__global__ __launch_bounds__(kNormBlock) void rmsnorm_mxfp8_kernel(const void* __restrict__ x,
+                                                                  const float* __restrict__ gain, int64_t d,
+                                                                  float eps, void* __restrict__ y_norm,
+                                                                  uint8_t* __restrict__ q,
+                                                                  uint8_t* __restrict__ scale) {
+    __shared__ float red[kNormBlock / 64];
+    const int64_t t = blockIdx.x;
+    const int64_t nch = d / 8;   // 8-channel chunks
+    float ss = 0.f;
+    for (int64_t c = threadIdx.x; c < nch; c += kNormBlock) {
+        Vec8<kBf16> v;
+        v.load(x, t * d + c * 8);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss = fmaf(v.v[i], v.v[i], ss);
+    }
+    // block sum: within the wave, then across the 4 waves
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kNormBlock / 64; ++w) tot += red[w];
+    const float r = 1.0f / sqrtf(tot / (float)d + eps);
+
+    const bool cast = q != nullptr;   // the host validates that q and scale come together
+    for (int64_t c0 = 0; c0 < nch; c0 += kNormBlock) {   // uniform loop: quads stay whole
+        const int64_t c = c0 + threadIdx.x;
+        const bool live = c < nch;
+        Vec8<kBf16> v;
+        if (live) {
+            v.load(x, t * d + c * 8);
+            const float4* gp = reinterpret_cast<const float4*>(gain + c * 8);
+            const float4 g0 = gp[0], g1 = gp[1];
+            const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v.v[i] = v.v[i] * r * gv[i];
+            v.round();   // the normalised row in its dtype
+            if (y_norm) v.store(y_norm, t * d + c * 8);
+        } else {
+            v.zero();
+        }
+        if (cast) {   // d % 32 == 0: a group's 4 chunks are all live or all dead
+            float a = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v.v[i]));
+            a = fmaxf(a, dpp<kQuadSwap1>(a));
+            a = fmaxf(a, dpp<kQuadSwap2>(a));
+            const int k = mx_scale_exp(a);
+            const float inv_s = __uint_as_float((uint32_t)(127 - k) << 23);   // 2^-k, exact
+            uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float sv = fminf(fmaxf(v.v[i] * inv_s, -448.f), 448.f);
+                const uint32_t code = e4m3_code(sv);
+                if (i < 4) w0 |= code << (8 * i);
+                else w1 |= code << (8 * (i - 4));
+            }
+            if (live) {
+                *reinterpret_cast<uint2*>(q + t * d + c * 8) = make_uint2(w0, w1);
+                if ((c & 3) == 0) scale[t * (d / 32) + c / 4] = (uint8_t)(k + 127);
+            }
+        }
+    }
+}
+
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace
@@ -1057,6 +1163,17 @@ void launch_pass_t(const PassArgs& a, const PassPlan& p, hipStream_t stream) {
                        stream, a);
 }
 }  // namespace
+
+hipError_t launch_rmsnorm_mxfp8(const void* x, bool bf16, const float* gain, int64_t n, int64_t d, float eps,
+                                void* y_norm, uint8_t* q, uint8_t* scale, hipStream_t stream) {
+    if (bf16)
+        hipLaunchKernelGGL(rmsnorm_mxfp8_kernel<true>, dim3((unsigned)n), dim3(kNormBlock), 0, stream, x, gain, d, eps,
+                           y_norm, q, scale);
+    else
+        hipLaunchKernelGGL(rmsnorm_mxfp8_kernel<false>, dim3((unsigned)n), dim3(kNormBlock), 0, stream, x, gain, d,
+                           eps, y_norm, q, scale);
+    return hipGetLastError();
+}
 
 hipError_t launch_pass_and_finalize(const PassRequest& r, hipStream_t stream) {
     const PassPlan p = plan_pass(r.n, r.d, r.bf16);

@@ -15,7 +15,8 @@
  *       Sinkhorn kernel and its wrapper), released configuration.
  *   "DeepSeek-V4.1-Flash" diagram -- blocks "Mixing Coefficients", "sigma",
  *       "x + eps_hc", "2 sigma", "First Sinkhorn Round", "Sinkhorn Round",
- *       "Cast", "Single-Pass mHC".
+ *       "Cast", "Single-Pass mHC", "Cast to MXFP8".
+ *   "DeepSeek-R1 donor reference" -- RMSNorm passages.
  *
  * Conventions shared by every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller; the library
@@ -131,6 +132,29 @@ int hc_pre(const void* x, int dtype, const float* pre_mix, int64_t n, int hc, in
  */
 int hc_post(const void* f, const void* residual, int dtype, const float* post,
             const float* comb, int64_t n, int hc, int64_t d, void* out, void* stream);
+
+/*
+ * The sublayer RMSNorm of the collapsed input and its MXFP8 cast -- atlas
+ * "Block", Block.forward (attn_norm / ffn_norm = RMSNorm(dim, norm_eps) on the
+ * output of hc_pre); "DeepSeek-R1 donor reference", RMSNorm passages (scale by
+ * 1/sqrt(mean x^2 + eps), multiply by the learned gain, restore the dtype);
+ * diagram "Single-Pass mHC" (the hidden state is normalised) and "Cast to
+ * MXFP8".
+ *   y_norm[t][e] = dtype( x[t][e] / sqrt(mean_e x[t][e]^2 + norm_eps) * gain[e] )
+ * and, for each group of 32 channels of a row of y_norm, with a = max |y_norm|
+ * over the group:
+ *   k = ceil(log2(max(a, 1e-4) / 448)),  scale[t][g] = k + 127 (UE8M0 byte),
+ *   q[t][32g + i] = E4M3( clamp(y_norm[t][32g + i] / 2^k, -448, 448) )
+ * (nearest E4M3 code, ties to even; sign kept).
+ *   x [n][d] dtype, gain [d] fp32 in; y_norm [n][d] dtype, q [n][d] uint8,
+ *   scale [n][d/32] uint8 out. y_norm may be NULL (the normalised row is then
+ *   only cast); q and scale are both NULL (no cast) or both given; at least one
+ *   output is required (HC_ERR_ARG otherwise). y_norm == x is allowed.
+ *   d % 8 == 0, and d % 32 == 0 when casting (HC_ERR_UNSUPPORTED otherwise);
+ *   q needs 8-byte alignment, scale any alignment; n < 2^31.
+ */
+int hc_rmsnorm_mxfp8(const void* x, int dtype, const float* gain, int64_t n, int64_t d,
+                     float norm_eps, void* y_norm, uint8_t* q, uint8_t* scale, void* stream);
 
 /*
  * One sublayer boundary of the single-pass design -- atlas "Block",

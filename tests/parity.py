@@ -33,7 +33,12 @@ def max_rel_err(got: torch.Tensor, ref: torch.Tensor, rho="row", tokens_dims=1) 
         rho_t = r2.pow(2).mean(1, keepdim=True).sqrt()
     else:
         rho_t = torch.full((lead, 1), float(rho), dtype=torch.float64)
-    return ((g2 - r2).abs() / torch.maximum(r2.abs(), rho_t)).max().item()
+    den = torch.maximum(r2.abs(), rho_t)
+    diff = (g2 - r2).abs()
+    # an all-zero reference row (den == 0) must be matched exactly
+    ratio = torch.where(den > 0, diff / den.clamp_min(1e-300),
+                        torch.where(diff > 0, torch.full_like(diff, float("inf")), torch.zeros_like(diff)))
+    return ratio.max().item()
 
 
 def check(name: str, got, ref, tol: float, rho="row", tokens_dims=1) -> float:

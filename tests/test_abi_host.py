@@ -31,13 +31,13 @@ C = 0x30000000
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^[a-z_ ]+[ *]+(hc_[a-z_]+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^[a-z_ ]+[ *]+(hc_[a-z_0-9]+)\s*\(", text, flags=re.M)))
 
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("hc_mixes", "hc_split_sinkhorn", "hc_pre", "hc_post", "hc_fused_step",
-                 "hc_workspace_size", "hc_status_string", "hc_abi_version"):
+                 "hc_rmsnorm_mxfp8", "hc_workspace_size", "hc_status_string", "hc_abi_version"):
         assert want in names
 
 
@@ -149,6 +149,28 @@ def test_fused_validation():
     assert _fused(f_prev=0x58000000, post_prev=0x59000000, comb_prev=0x59001000,
                   so=A + 16) == ALIAS                              # partial overlap with residual
     assert _fused(mixes=0x70000080) == ALIAS                       # mixes inside pre
+
+
+def _norm(x=A, dtype=1, gain=B, n=16, d=256, eps=1e-20, y=C, q=0x40000000, sc=0x50000000):
+    return hc.lib().hc_rmsnorm_mxfp8(P(x), dtype, P(gain), n, d, eps, P(y), P(q), P(sc), None)
+
+
+def test_rmsnorm_mxfp8_validation():
+    assert _norm(n=0) == OK
+    assert _norm(n=-1) == SHAPE
+    assert _norm(d=4) == SHAPE
+    assert _norm(d=(1 << 20) + 32) == SHAPE
+    assert _norm(d=260) == UNSUP                        # d % 8
+    assert _norm(d=264) == UNSUP                        # cast needs d % 32 == 0
+    assert _norm(dtype=5) == UNSUP
+    assert _norm(eps=-1.0) == ARG
+    assert _norm(y=None, q=None, sc=None) == ARG         # nothing requested
+    assert _norm(sc=None) == NULL                        # codes without scales
+    assert _norm(x=None) == NULL
+    assert _norm(q=0x40000004) == ALIGN
+    assert _norm(y=A + 16) == ALIAS                      # partial overlap with x
+    assert _norm(q=A + 64) == ALIAS                      # codes inside x
+    assert _norm(sc=0x40000000 + 16 * 256 - 8) == ALIAS  # scales inside codes
 
 
 @pytest.mark.parametrize("fn", ["hc_pre", "hc_post", "hc_mixes", "hc_fused_step"])

@@ -244,3 +244,60 @@ def test_long_prefill_40_layers_sampled_tokens():
     check("last collapse (sampled)", cpu_rows(y), ref_y, TOL_BF16)
     for name, g, rr in (("last pre", pi, ref_pi), ("last post", post, ref_post), ("last comb", comb, ref_comb)):
         check(f"{name} (sampled)", cpu_rows(g), rr, TOL_BF16, rho=1.0)
+
+
+# ------------------------------------------------- RMSNorm + MXFP8 cast (next rows)
+def _norm_case(dtype, n, d, seed=21):
+    """Collapsed-input stand-ins: N(0, 1) rows, rows with a per-element magnitude
+    spread of four decades (subnormal E4M3 codes), one row below the 1e-4 scale
+    floor, one all-zero row, one large row; gain ~ U(-1.5, 1.5)."""
+    g = hc_inputs.generator(seed)
+    x = hc_inputs.normal(g, (n, d))
+    if n >= 4:
+        spread = torch.pow(10.0, -4.0 * torch.rand(n // 4, d, generator=g))
+        x[: n // 4] *= spread
+        x[-1] *= 1e-7
+        x[-2] = 0.0
+        x[-3] *= 3e4
+    gain = torch.rand(d, generator=g) * 3.0 - 1.5
+    return x.to(dtype), gain
+
+
+@pytest.mark.parametrize("dtype,n,d", [(torch.bfloat16, 37, 288), (torch.bfloat16, 1, 32),
+                                       (torch.float32, 16, 256), (torch.bfloat16, 4096, 5120)])
+def test_rmsnorm_mxfp8(dtype, n, d):
+    """Normalised rows within the stream tolerance of the oracle; E4M3 codes and
+    UE8M0 scales bit-exact against the oracle's cast of the same normalised rows
+    (the cast's integer decisions are taken on identical inputs)."""
+    x, gain = _norm_case(dtype, n, d)
+    xd, gd = to_dev((x, gain))
+    r = hc.rmsnorm_mxfp8(xd, gd)
+    sync()
+    check(f"rmsnorm {dtype} {n}x{d}", r["y_norm"], oracle.rmsnorm(x, gain),
+          TOL_F32 if dtype == torch.float32 else TOL_BF16)
+    q_ref, s_ref = oracle.mxfp8(r["y_norm"].cpu())
+    assert torch.equal(r["scale"].cpu(), s_ref), "UE8M0 scales differ"
+    q = r["q"].cpu()
+    bad = (q != q_ref).sum().item()
+    assert bad == 0, f"{bad} E4M3 codes differ"
+    # cast only, and in place: identical results
+    r2 = hc.rmsnorm_mxfp8(xd, gd, want_norm=False)
+    hc.rmsnorm_mxfp8(xd, gd, want_cast=False, y_norm=xd)
+    sync()
+    assert torch.equal(r2["q"], r["q"]) and torch.equal(r2["scale"], r["scale"])
+    assert torch.equal(xd, r["y_norm"])
+
+
+def test_rmsnorm_mxfp8_after_collapse():
+    """The chain the next rows serve: prefill attention boundary (fused step) ->
+    RMSNorm -> MXFP8 of its collapsed input, against the oracle on the same y."""
+    inp = hc_inputs.prefill(seed=2)
+    pi = oracle_pi(inp)
+    a = hc.hc_fused_step(*to_dev((inp["x"],)), *to_dev(inp["attn"]), pre_mix=to_dev(pi))
+    gain = torch.rand(inp["x"].shape[-1], generator=hc_inputs.generator(9)) + 0.5
+    r = hc.rmsnorm_mxfp8(a["y"], to_dev(gain))
+    sync()
+    y = a["y"].cpu()
+    check("rmsnorm(y)", r["y_norm"], oracle.rmsnorm(y, gain), TOL_BF16)
+    q_ref, s_ref = oracle.mxfp8(r["y_norm"].cpu())
+    assert torch.equal(r["scale"].cpu(), s_ref) and torch.equal(r["q"].cpu(), q_ref)
