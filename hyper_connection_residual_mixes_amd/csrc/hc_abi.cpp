@@ -126,7 +126,7 @@ int hc_rmsnorm_mxfp8(const void* x, int dtype, const float* gain, int64_t n, int
                      void* y_norm, uint8_t* q, uint8_t* scale, void* stream) {
     if (n < 0 || d < 8 || d > (int64_t(1) << 20)) return HC_ERR_SHAPE;
     if (n > 0 && (uint64_t)d > (uint64_t(1) << 40) / (uint64_t)n) return HC_ERR_SHAPE;
-    if (n > 0x7fffffff) return HC_ERR_SHAPE;                     // one workgroup per row
+    if (n > 0x7fffffff) return HC_ERR_SHAPE;                     // the documented row bound
     if (dtype != HC_F32 && dtype != HC_BF16) return HC_ERR_UNSUPPORTED;
     if (d % 8 != 0) return HC_ERR_UNSUPPORTED;
     if (check_eps(norm_eps) != HC_OK) return HC_ERR_ARG;

@@ -989,11 +989,11 @@ __global__ __launch_bounds__(kSwBlock) void bf16_sweep_kernel(PassArgs a) {
 // ------------------------------------------- sublayer RMSNorm + MXFP8 cast
 // The sublayer input after the collapse is RMS-normalised with a learned gain
 // (Block.forward: attn_norm / ffn_norm) and cast to MXFP8 for the projections
-// that read it (diagram "Cast to MXFP8"). One workgroup per token row: pass 1
-// sums the squares of the row; pass 2 re-reads it (L1/L2 hit), multiplies by
-// 1/sqrt(mean + eps) and the gain, rounds to the row dtype (the normalised
-// output), and casts groups of 32 channels: four consecutive lanes own a group
-// (8 channels each), its amax is combined with two quad DPP steps.
+// that read it (diagram "Cast to MXFP8"). Pass 1 sums the squares of a row;
+// pass 2 multiplies by 1/sqrt(mean + eps) and the gain, rounds to the row dtype
+// (the normalised output), and casts groups of 32 channels: four consecutive
+// lanes own a group (8 channels each), its amax is combined with two quad DPP
+// steps.
 constexpr int kNormBlock = 256;
 
 // ceil(log2(max(a, 1e-4) / 448)) for a >= 0, exactly: 448 = 1.75 * 2^8, so for
@@ -1004,87 +1004,252 @@ __device__ __forceinline__ int mx_scale_exp(float a) {
     return e - 8 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0);
 }
 
-// E4M3 code of v (|v| <= 448): nearest code, ties to the even code, sign kept.
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-    const uint32_t bits = __float_as_uint(v);
-    const uint32_t sign = (bits >> 24) & 0x80u;
-    const float a = fabsf(v);
-    if (a < 0.015625f)   // below 2^-6: subnormal codes, multiples of 2^-9 (code 8 = 2^-6)
-        return sign | (uint32_t)__builtin_rintf(a * 512.0f);
-    const uint32_t ab = __float_as_uint(a);
-    uint32_t exp = (ab >> 23) - 127 + 7;            // biased E4M3 exponent, 1..15
-    uint32_t mant = (ab >> 20) & 7u;
-    const uint32_t rest = ab & 0xfffffu, half = 0x80000u;
-    if (rest > half || (rest == half && (mant & 1u))) ++mant;
-    if (mant == 8u) {
-        mant = 0;
-        ++exp;
+// A wave normalises a row at a time, rows taken grid-stride by up to
+// kNormWaves waves (more than are resident, for balance). Lane l owns 8-channel
+// chunks l, l + 64, ...; the row's sum of squares is a wave reduction and a
+// 32-channel group is 4 consecutive lanes. When the row fits (kChunks > 0 chunks
+// per lane) it stays in registers between the two passes, every load of a row is
+// issued before the first wait, and the gain is staged once per workgroup in
+// LDS; the register budget leaves room for four waves per SIMD, which keeps a
+// whole 4096-row batch in flight. Every access is a raw buffer access whose
+// range is the row (or zero for an absent output), so masked lanes and absent
+// outputs cost no branch: the body is straight-line and the compiler's
+// memory-counter waits stay exact. Wider rows (kChunks == 0) stream the row
+// twice and read the gain from memory.
+constexpr int kNormRows = kNormBlock / 64;   // waves per workgroup
+constexpr int kNormWaves = 8192;             // at most 32 waves per CU on 256 CUs
+// float4 of the staged gain each thread loads: 2 per 8-channel chunk
+__host__ __device__ constexpr int norm_gain_per_thread(int chunks) { return (chunks * 128 + kNormBlock - 1) / kNormBlock; }
+template <bool kBf16>
+constexpr int kNormMaxChunks = kBf16 ? 16 : 8;   // at most 64 VGPRs of row per lane
+// s_waitcnt immediate that waits for vmcnt <= n only (vmcnt in bits 3:0 and
+// 15:14; expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+__host__ __device__ constexpr int waitcnt_vm(int n) { return ((n >> 4) << 14) | (0xF << 8) | (7 << 4) | (n & 15); }
+
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// 8 channels as loaded: bf16 one 16-byte word, fp32 two.
+template <bool kBf16>
+struct NormChunk {
+    uint4 w[kBf16 ? 1 : 2];
+
+    __device__ __forceinline__ static uint32_t word(const uint4& u, int i) {
+        return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
     }
-    return sign | (exp << 3) | mant;
+    __device__ __forceinline__ float get(int i) const {   // i is a compile-time constant after unrolling
+        if constexpr (kBf16) {
+            const uint32_t u = word(w[0], i >> 1);
+            return (i & 1) ? bf16_hi(u) : bf16_lo(u);
+        } else {
+            return __uint_as_float(word(w[i >> 2], i & 3));
+        }
+    }
+};
+
+// Buffer resources of one row: x (read), y_norm, q and scale (written). A row
+// past n, or an output not asked for, gets an empty range.
+struct NormRowRsrc {
+    __amdgpu_buffer_rsrc_t x, y, q, s;
+};
+
+template <bool kBf16>
+__device__ __forceinline__ NormRowRsrc norm_row_rsrc(const void* x, void* y_norm, uint8_t* q, uint8_t* scale,
+                                                     int64_t t, int64_t n, int64_t d) {
+    constexpr int64_t kElem = kBf16 ? 2 : 4;
+    const bool ok = t < n;
+    const int64_t tt = ok ? t : 0;
+    NormRowRsrc r;
+    r.x = make_rsrc(static_cast<const uint8_t*>(x) + tt * d * kElem, ok ? d * kElem : 0);
+    r.y = make_rsrc(y_norm ? static_cast<uint8_t*>(y_norm) + tt * d * kElem : nullptr, ok && y_norm ? d * kElem : 0);
+    r.q = make_rsrc(q ? q + tt * d : nullptr, ok && q ? d : 0);
+    r.s = make_rsrc(q ? scale + tt * (d / 32) : nullptr, ok && q ? d / 32 : 0);
+    return r;
+}
+
+// Byte offset of chunk c within a row, or kOffMasked past the row end.
+template <bool kBf16>
+__device__ __forceinline__ uint32_t norm_chunk_off(uint32_t c, uint32_t nch) {
+    return c < nch ? c * (kBf16 ? 16u : 32u) : kOffMasked;
 }
 
 template <bool kBf16>
+__device__ __forceinline__ void norm_load(NormChunk<kBf16>& xc, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    xc.w[0] = buf_load16(r, off, 0);
+    if constexpr (!kBf16) xc.w[1] = buf_load16(r, off + 16, 0);   // a masked offset stays out of range
+}
+
+template <bool kBf16, int kChunks>
+__device__ __forceinline__ void norm_load_row(NormChunk<kBf16> (&xc)[kChunks], __amdgpu_buffer_rsrc_t r,
+                                              uint32_t lane, uint32_t nch) {
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) norm_load<kBf16>(xc[i], r, norm_chunk_off<kBf16>(lane + i * 64, nch));
+}
+
+// Sum of squares of a chunk (chunks past the row end were loaded as zeros).
+// bf16: one dot2 per packed word (the squares of bf16 values are exact in fp32).
+template <bool kBf16>
+__device__ __forceinline__ void norm_sumsq(const NormChunk<kBf16>& xc, float& ss) {
+    if constexpr (kBf16) {
+        const uint32_t w[4] = {xc.w[0].x, xc.w[0].y, xc.w[0].z, xc.w[0].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bf16x2_t b = __builtin_bit_cast(bf16x2_t, w[i]);
+            ss = __builtin_amdgcn_fdot2_f32_bf16(b, b, ss, false);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = fmaf(xc.get(e), xc.get(e), ss);
+    }
+}
+
+__device__ __forceinline__ void buf_store8(u32x2_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)voff, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 1");   // the same two wait states as buf_store16
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Pass 2 for chunk c of a row: scale by r and the gain (g0, g1), round to the
+// row dtype, store the normalised values, and cast the chunk's share of its
+// 32-channel group. Stores of a chunk past the row end use a masked offset; a
+// dead lane's quad is all dead (d % 32 == 0 when casting), so whatever it
+// computes is dropped.
+template <bool kBf16>
+__device__ __forceinline__ void norm_cast_chunk(const NormChunk<kBf16>& xc, float4 g0, float4 g1, float r,
+                                                uint32_t c, uint32_t nch, const NormRowRsrc& rr) {
+    const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    Vec8<kBf16> v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v.v[i] = xc.get(i) * r * gv[i];
+    // amax of the rounded values: rounding to nearest is monotonic, so it is the
+    // rounded amax of the fp32 values
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v.v[i]));
+    if constexpr (kBf16) a = bf16_lo(pack_bf16x2(a, 0.f));
+    v.round();   // the normalised row in its dtype
+    const uint32_t off = norm_chunk_off<kBf16>(c, nch);
+    if constexpr (kBf16) {
+        buf_store16(v.raw, rr.y, off, 0);
+    } else {
+        buf_store16(make_uint4(__float_as_uint(v.v[0]), __float_as_uint(v.v[1]), __float_as_uint(v.v[2]),
+                               __float_as_uint(v.v[3])),
+                    rr.y, off, 0);
+        buf_store16(make_uint4(__float_as_uint(v.v[4]), __float_as_uint(v.v[5]), __float_as_uint(v.v[6]),
+                               __float_as_uint(v.v[7])),
+                    rr.y, off + 16, 0);
+    }
+    a = fmaxf(a, dpp<kQuadSwap1>(a));
+    a = fmaxf(a, dpp<kQuadSwap2>(a));
+    const int k = mx_scale_exp(a);
+    // |v| <= amax <= 448 * 2^k, so the scaled values need no clamp. The hardware
+    // packs (two codes per instruction) round v / 2^k to the nearest OCP E4M3
+    // code, ties to the even code, sign kept, the subnormal codes (multiples of
+    // 2^-9 below 2^-6) included; the bf16 form reads the packed words directly.
+    uint32_t w0, w1;
+    if constexpr (kBf16) {
+        const float sc = __uint_as_float((uint32_t)(127 + k) << 23);   // 2^k, exact
+        typedef short s16x2_t __attribute__((ext_vector_type(2)));
+        const uint32_t raw[4] = {v.raw.x, v.raw.y, v.raw.z, v.raw.w};
+        s16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(s16x2_t{0, 0}, __builtin_bit_cast(bf16x2_t, raw[0]),
+                                                               sc, false);
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(lo, __builtin_bit_cast(bf16x2_t, raw[1]), sc, true);
+        s16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(s16x2_t{0, 0}, __builtin_bit_cast(bf16x2_t, raw[2]),
+                                                               sc, false);
+        hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hi, __builtin_bit_cast(bf16x2_t, raw[3]), sc, true);
+        w0 = __builtin_bit_cast(uint32_t, lo);
+        w1 = __builtin_bit_cast(uint32_t, hi);
+    } else {
+        const float inv_s = __uint_as_float((uint32_t)(127 - k) << 23);   // 2^-k, exact
+        w0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v.v[0] * inv_s, v.v[1] * inv_s, 0, false);
+        w0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v.v[2] * inv_s, v.v[3] * inv_s, (int)w0, true);
+        w1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v.v[4] * inv_s, v.v[5] * inv_s, 0, false);
+        w1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v.v[6] * inv_s, v.v[7] * inv_s, (int)w1, true);
+    }
+    buf_store8(u32x2_t{w0, w1}, rr.q, c < nch ? c * 8 : kOffMasked);
+    __builtin_amdgcn_raw_buffer_store_b8((unsigned char)(k + 127), rr.s, (c < nch && (c & 3) == 0) ? c / 4 : kOffMasked,
+                                         0, 0);
+}
+
+template <bool kBf16, int kChunks>
+__device__ __forceinline__ void norm_process_row(const NormChunk<kBf16> (&xc)[kChunks], const float4* gain_lds,
+                                                 float eps, int64_t d, uint32_t lane, uint32_t nch,
+                                                 const NormRowRsrc& rr) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) norm_sumsq<kBf16>(xc[i], ss);
+    const float r = 1.0f / sqrtf(wave_sum(ss) / (float)d + eps);
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+        const uint32_t c = lane + i * 64;
+        const uint32_t cg = c < nch ? c : nch - 1;
+        norm_cast_chunk<kBf16>(xc[i], gain_lds[2 * cg], gain_lds[2 * cg + 1], r, c, nch, rr);
+    }
+}
+
+template <bool kBf16, int kChunks>
 __global__ __launch_bounds__(kNormBlock) void rmsnorm_mxfp8_kernel(const void* __restrict__ x,
-                                                                  const float* __restrict__ gain, int64_t d,
-                                                                  float eps, void* __restrict__ y_norm,
+                                                                  const float* __restrict__ gain, int64_t n,
+                                                                  int64_t d, float eps, void* __restrict__ y_norm,
                                                                   uint8_t* __restrict__ q,
                                                                   uint8_t* __restrict__ scale) {
-    __shared__ float red[kNormBlock / 64];
-    const int64_t t = blockIdx.x;
-    const int64_t nch = d / 8;   // 8-channel chunks
-    float ss = 0.f;
-    for (int64_t c = threadIdx.x; c < nch; c += kNormBlock) {
-        Vec8<kBf16> v;
-        v.load(x, t * d + c * 8);
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t nw = (int64_t)gridDim.x * kNormRows;
+    const uint32_t nch = (uint32_t)(d / 8);
+    int64_t ta = (int64_t)blockIdx.x * kNormRows + wave;
+    if constexpr (kChunks > 0) {
+        extern __shared__ float4 gain_lds[];   // kGainPer * kNormBlock entries: the gain, padded
+        constexpr int kGainPer = norm_gain_per_thread(kChunks);
+        // Stage the gain straight into LDS (a 16-byte load per lane, written at
+        // the wave's base + 16 * lane), ahead of the row loads; entries past the
+        // gain repeat its last float4 and are never read.
+        const uint32_t ng = nch * 2;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ss = fmaf(v.v[i], v.v[i], ss);
-    }
-    // block sum: within the wave, then across the 4 waves
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    float tot = 0.f;
-#pragma unroll
-    for (int w = 0; w < kNormBlock / 64; ++w) tot += red[w];
-    const float r = 1.0f / sqrtf(tot / (float)d + eps);
-
-    const bool cast = q != nullptr;   // the host validates that q and scale come together
-    for (int64_t c0 = 0; c0 < nch; c0 += kNormBlock) {   // uniform loop: quads stay whole
-        const int64_t c = c0 + threadIdx.x;
-        const bool live = c < nch;
-        Vec8<kBf16> v;
-        if (live) {
-            v.load(x, t * d + c * 8);
-            const float4* gp = reinterpret_cast<const float4*>(gain + c * 8);
-            const float4 g0 = gp[0], g1 = gp[1];
-            const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v.v[i] = v.v[i] * r * gv[i];
-            v.round();   // the normalised row in its dtype
-            if (y_norm) v.store(y_norm, t * d + c * 8);
-        } else {
-            v.zero();
+        for (int j = 0; j < kGainPer; ++j) {
+            const uint32_t k = threadIdx.x + j * kNormBlock;
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)(reinterpret_cast<const float4*>(gain) +
+                                                                (k < ng ? k : ng - 1)),
+                (__attribute__((address_space(3))) void*)(gain_lds + j * kNormBlock + wave * 64), 16, 0, 0);
         }
-        if (cast) {   // d % 32 == 0: a group's 4 chunks are all live or all dead
-            float a = 0.f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v.v[i]));
-            a = fmaxf(a, dpp<kQuadSwap1>(a));
-            a = fmaxf(a, dpp<kQuadSwap2>(a));
-            const int k = mx_scale_exp(a);
-            const float inv_s = __uint_as_float((uint32_t)(127 - k) << 23);   // 2^-k, exact
-            uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float sv = fminf(fmaxf(v.v[i] * inv_s, -448.f), 448.f);
-                const uint32_t code = e4m3_code(sv);
-                if (i < 4) w0 |= code << (8 * i);
-                else w1 |= code << (8 * (i - 4));
+        __builtin_amdgcn_sched_barrier(0);   // keep the staging loads ahead of the row loads
+        constexpr int kLoadsPerRow = kChunks * (kBf16 ? 1 : 2);
+        NormChunk<kBf16> xc[kChunks];
+        NormRowRsrc rr = norm_row_rsrc<kBf16>(x, y_norm, q, scale, ta, n, d);
+        norm_load_row<kBf16, kChunks>(xc, rr.x, lane, nch);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoadsPerRow));   // the staging loads (issued first) are done
+        __syncthreads();                                        // ... in every wave
+        while (ta < n) {
+            norm_process_row<kBf16, kChunks>(xc, gain_lds, eps, d, lane, nch, rr);
+            ta += nw;
+            if (ta >= n) break;
+            rr = norm_row_rsrc<kBf16>(x, y_norm, q, scale, ta, n, d);
+            norm_load_row<kBf16, kChunks>(xc, rr.x, lane, nch);
+        }
+    } else {
+        const float4* gv = reinterpret_cast<const float4*>(gain);
+        for (; ta < n; ta += nw) {
+            const NormRowRsrc rr = norm_row_rsrc<kBf16>(x, y_norm, q, scale, ta, n, d);
+            NormChunk<kBf16> xc;
+            float ss = 0.f;
+            for (uint32_t c = lane; c < nch; c += 64) {
+                norm_load<kBf16>(xc, rr.x, norm_chunk_off<kBf16>(c, nch));
+                norm_sumsq<kBf16>(xc, ss);
             }
-            if (live) {
-                *reinterpret_cast<uint2*>(q + t * d + c * 8) = make_uint2(w0, w1);
-                if ((c & 3) == 0) scale[t * (d / 32) + c / 4] = (uint8_t)(k + 127);
+            const float r = 1.0f / sqrtf(wave_sum(ss) / (float)d + eps);
+            for (uint32_t c0 = 0; c0 < nch; c0 += 64) {   // uniform trip count: quads stay whole
+                const uint32_t c = c0 + lane;
+                const uint32_t cg = c < nch ? c : nch - 1;
+                norm_load<kBf16>(xc, rr.x, norm_chunk_off<kBf16>(c, nch));
+                norm_cast_chunk<kBf16>(xc, gv[2 * cg], gv[2 * cg + 1], r, c, nch, rr);
             }
         }
     }
@@ -1164,14 +1329,39 @@ void launch_pass_t(const PassArgs& a, const PassPlan& p, hipStream_t stream) {
 }
 }  // namespace
 
+template <bool kBf16, int kChunks>
+void launch_norm(dim3 grid, const void* x, const float* gain, int64_t n, int64_t d, float eps, void* y_norm,
+                 uint8_t* q, uint8_t* scale, hipStream_t stream) {
+    const size_t lds = (size_t)norm_gain_per_thread(kChunks) * kNormBlock * sizeof(float4);   // the staged gain
+    hipLaunchKernelGGL((rmsnorm_mxfp8_kernel<kBf16, kChunks>), grid, dim3(kNormBlock), lds, stream, x, gain, n, d,
+                       eps, y_norm, q, scale);
+}
+
+template <bool kBf16>
+void launch_norm_dtype(dim3 grid, const void* x, const float* gain, int64_t n, int64_t d, float eps, void* y_norm,
+                       uint8_t* q, uint8_t* scale, hipStream_t stream) {
+    // chunks per lane, rounded up to an even count (one instance per even count)
+    const int64_t need = ceil_div(d / 8, 64);
+    switch (need <= kNormMaxChunks<kBf16> ? (need + 1) / 2 * 2 : 0) {
+        case 2: return launch_norm<kBf16, 2>(grid, x, gain, n, d, eps, y_norm, q, scale, stream);
+        case 4: return launch_norm<kBf16, 4>(grid, x, gain, n, d, eps, y_norm, q, scale, stream);
+        case 6: return launch_norm<kBf16, 6>(grid, x, gain, n, d, eps, y_norm, q, scale, stream);
+        case 8: return launch_norm<kBf16, 8>(grid, x, gain, n, d, eps, y_norm, q, scale, stream);
+        case 10: return launch_norm<kBf16, kBf16 ? 10 : 0>(grid, x, gain, n, d, eps, y_norm, q, scale, stream);
+        case 12: return launch_norm<kBf16, kBf16 ? 12 : 0>(grid, x, gain, n, d, eps, y_norm, q, scale, stream);
+        case 14: return launch_norm<kBf16, kBf16 ? 14 : 0>(grid, x, gain, n, d, eps, y_norm, q, scale, stream);
+        case 16: return launch_norm<kBf16, kBf16 ? 16 : 0>(grid, x, gain, n, d, eps, y_norm, q, scale, stream);
+        default: return launch_norm<kBf16, 0>(grid, x, gain, n, d, eps, y_norm, q, scale, stream);
+    }
+}
+
 hipError_t launch_rmsnorm_mxfp8(const void* x, bool bf16, const float* gain, int64_t n, int64_t d, float eps,
                                 void* y_norm, uint8_t* q, uint8_t* scale, hipStream_t stream) {
+    const dim3 grid((unsigned)ceil_div(n < kNormWaves ? n : kNormWaves, kNormRows));   // rows grid-stride
     if (bf16)
-        hipLaunchKernelGGL(rmsnorm_mxfp8_kernel<true>, dim3((unsigned)n), dim3(kNormBlock), 0, stream, x, gain, d, eps,
-                           y_norm, q, scale);
+        launch_norm_dtype<true>(grid, x, gain, n, d, eps, y_norm, q, scale, stream);
     else
-        hipLaunchKernelGGL(rmsnorm_mxfp8_kernel<false>, dim3((unsigned)n), dim3(kNormBlock), 0, stream, x, gain, d,
-                           eps, y_norm, q, scale);
+        launch_norm_dtype<false>(grid, x, gain, n, d, eps, y_norm, q, scale, stream);
     return hipGetLastError();
 }
 

@@ -263,8 +263,13 @@ def _norm_case(dtype, n, d, seed=21):
     return x.to(dtype), gain
 
 
+# Rows of up to 16 (bf16) / 8 (fp32) 8-channel chunks per lane stay in registers;
+# wider rows (8224 bf16, 4128 and 8224 fp32) take the streamed path. Beyond 8192
+# rows a wave takes several rows in turn (the 8229- and 8195-row cases).
 @pytest.mark.parametrize("dtype,n,d", [(torch.bfloat16, 37, 288), (torch.bfloat16, 1, 32),
-                                       (torch.float32, 16, 256), (torch.bfloat16, 4096, 5120)])
+                                       (torch.float32, 16, 256), (torch.bfloat16, 4096, 5120),
+                                       (torch.bfloat16, 9, 8224), (torch.float32, 5, 8224),
+                                       (torch.bfloat16, 8229, 256), (torch.float32, 8195, 4128)])
 def test_rmsnorm_mxfp8(dtype, n, d):
     """Normalised rows within the stream tolerance of the oracle; E4M3 codes and
     UE8M0 scales bit-exact against the oracle's cast of the same normalised rows
