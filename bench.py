@@ -203,7 +203,8 @@ def main():
     next_rows = {"rmsnorm_mxfp8": {
         "workload": f"RMSNorm (gain) + MXFP8 cast of the collapsed input, {n} x {d} bf16 -> E4M3 + UE8M0",
         "kernel": "rmsnorm_mxfp8_kernel", "us": norm_us, "algorithmic_bytes": norm_bytes,
-        "achieved_gb_s": norm_bytes / norm_us / 1e3, "frac": norm_bytes / norm_us / 1e3 / PEAK_HBM_GBS}}
+        "achieved_gb_s": norm_bytes / norm_us / 1e3, "frac": norm_bytes / norm_us / 1e3 / PEAK_HBM_GBS,
+        "traffic": stored_traffic("rmsnorm_mxfp8")}}
 
     result = {
         "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
