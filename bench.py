@@ -93,6 +93,83 @@ def cpu_baseline(sets_cpu):
                        f"single-threaded C oracle in fp64, {dt:.1f} s")
 
 
+def decode_latency(dev, reps: int = 300):
+    """One decode block (64 tokens x 4 streams x 5120 bf16; attention boundary, FFN
+    boundary, FFN expand) called eagerly and replayed from a HIP graph of the same
+    three entry points, which takes the host-side launch path out. Every graph
+    replay is checked against the eager outputs. Returns the figures per block."""
+    import torch
+    import hc_inputs
+    import hyper_connection_residual_mixes_amd as hc
+    w = hc_inputs.DECODE
+    n, d = w.n, w.d
+    sets = []
+    for s in range(3):
+        inp = hc_inputs.decode(seed=s, device=dev)
+        pi, _, _ = hc.hc_split_sinkhorn(*inp["prev"])
+        out = dict(yA=torch.empty(n, d, dtype=w.dtype, device=dev), yF=torch.empty(n, d, dtype=w.dtype, device=dev),
+                   x1=torch.empty(n, 4, d, dtype=w.dtype, device=dev),
+                   x2=torch.empty(n, 4, d, dtype=w.dtype, device=dev),
+                   cA=tuple(torch.empty(sh, device=dev) for sh in ((n, 4), (n, 4), (n, 4, 4))),
+                   cF=tuple(torch.empty(sh, device=dev) for sh in ((n, 4), (n, 4), (n, 4, 4))))
+        sets.append((inp, pi, out))
+    ws = torch.empty(hc.workspace_size(n, 4, d), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        inp, pi, o = sets[i % 3]
+        a = hc.hc_fused_step(inp["x"], *inp["attn"], pre_mix=pi, y=o["yA"], out=o["cA"], workspace=ws)
+        f = hc.hc_fused_step(inp["x"], *inp["ffn"], pre_mix=a["pre"], f_prev=inp["f_attn"], post_prev=a["post"],
+                             comb_prev=a["comb"], streams_out=o["x1"], y=o["yF"], out=o["cF"], workspace=ws)
+        hc.hc_post(inp["f_ffn"], f["streams"], f["post"], f["comb"], out=o["x2"])
+
+    def outputs():
+        return [t for _, _, o in sets for t in (o["yA"], o["yF"], o["x1"], o["x2"], *o["cA"], *o["cF"])]
+
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        for i in range(30):
+            step(i)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outputs()]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(reps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    eager_wall = (time.perf_counter() - t0) / reps
+    eager_gpu = e0.elapsed_time(e1) * 1e-3 / reps
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(3):
+            step(i)
+    for _ in range(3):                       # replays, with eager work between them
+        for t in outputs():
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        if not all(torch.equal(a, b) for a, b in zip(ref, outputs())):
+            raise RuntimeError("decode block: a graph replay differs from the eager result")
+        step(0)
+        torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(reps // 3):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_wall = (time.perf_counter() - t0) / (reps // 3 * 3)
+    block_bytes = algorithmic_bytes(n, d)["block"]
+    return {"workload": f"decode block, {n} tokens x 4 streams x {d} bf16 (attention + FFN boundaries)",
+            "us_per_block_eager": eager_wall * 1e6, "us_per_block_eager_gpu": eager_gpu * 1e6,
+            "us_per_block_graph": graph_wall * 1e6, "tokens_per_s_graph": n / graph_wall,
+            "algorithmic_bytes": block_bytes, "achieved_gb_s_graph": block_bytes / graph_wall / 1e9}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -224,6 +301,7 @@ def main():
                                      "frac": ab[k] / per[k] / 1e9 / PEAK_HBM_GBS,
                                      "traffic": stored_traffic(k)} for k in per},
     }
+    next_rows["decode"] = decode_latency(dev)
     result["next_rows"] = next_rows
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on every input set", file=sys.stderr, flush=True)

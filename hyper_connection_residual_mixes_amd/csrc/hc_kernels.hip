@@ -638,24 +638,18 @@ struct FinalizeArgs {
     float* comb;
 };
 
-// Token t (shared by the 16-lane group; t >= n: computes on token 0, stores
-// nothing), lane e of the group. Every lane of the wave must call it.
-__device__ __forceinline__ void finalize16(const FinalizeArgs& f, int64_t t, int e) {
-    const bool ok = t < f.n;
-    const int64_t tt = ok ? t : 0;
-    // fixed-order reduction over the channel slices
-    float a0 = 0.f, a1 = 0.f;
-    for (int s = 0; s < f.nsplit; ++s) {
-        const float* p = f.part + ((int64_t)s * f.n + tt) * kPart;
-        a0 += p[e];
-        a1 += p[16 + e];                   // entries 16..31; 25..31 are never used below
-    }
+// The coefficients of token t from its reduced partial row: lane e of a 16-lane
+// group holds entries e (a0) and 16 + e (a1). Every lane of the wave must call it
+// (row and column sums are DPP steps within the group); only lanes with `store`
+// write.
+__device__ __forceinline__ void finalize_coeffs(const FinalizeArgs& f, int64_t t, int e, float a0, float a1,
+                                                bool store) {
     const int lane16 = (threadIdx.x & 63) & ~15;
     const float sumsq = __shfl(a1, lane16 + (kMix - 16));
     const float rstd = 1.0f / sqrtf(sumsq / (float)f.D + f.norm_eps);
     const float m0 = a0 * rstd;            // mixes[e]
     const float m1 = a1 * rstd;            // mixes[16 + e] (valid for e < 8)
-    if (f.mixes && ok) {
+    if (f.mixes && store) {
         f.mixes[t * kMix + e] = m0;
         if (e < kMix - 16) f.mixes[t * kMix + 16 + e] = m1;
     }
@@ -675,17 +669,75 @@ __device__ __forceinline__ void finalize16(const FinalizeArgs& f, int64_t t, int
         c *= __builtin_amdgcn_rcpf(row_sum16(c) + f.eps);
         c *= __builtin_amdgcn_rcpf(col_sum16(c) + f.eps);
     }
-    if (ok) {
+    if (store) {
         f.comb[t * 16 + e] = c;
         if (e < kHC) f.pre[t * kHC + e] = sigmoid(m0 * f.scale[0] + f.base[e]) + f.eps;
         else if (e < 2 * kHC) f.post[t * kHC + e - kHC] = 2.0f * sigmoid(m0 * f.scale[1] + f.base[e]);
     }
 }
 
+// 16 lanes per token: token t (shared by the 16-lane group; t >= n: computes on
+// token 0, stores nothing), lane e of the group reduces entries e and 16 + e over
+// the slices in order. Suits a few slices.
+__device__ __forceinline__ void finalize16(const FinalizeArgs& f, int64_t t, int e) {
+    const bool ok = t < f.n;
+    const int64_t tt = ok ? t : 0;
+    float a0 = 0.f, a1 = 0.f;
+    for (int s = 0; s < f.nsplit; ++s) {
+        const float* p = f.part + ((int64_t)s * f.n + tt) * kPart;
+        a0 += p[e];
+        a1 += p[16 + e];                   // entries 16..31; 25..31 are never used below
+    }
+    finalize_coeffs(f, t, e, a0, a1, ok);
+}
+
 constexpr int kFinBlock = 256;
 
 __global__ __launch_bounds__(kFinBlock) void finalize_kernel(FinalizeArgs f) {
     finalize16(f, ((int64_t)blockIdx.x * kFinBlock + threadIdx.x) >> 4, threadIdx.x & 15);
+}
+
+// A wave per token, for many slices: lane l reads float4 l % 8 (entries
+// 4 (l % 8) .. + 3) of slices l / 8, l / 8 + 8, ...; every load is issued before
+// the first wait, and slices past nsplit read as zero (masked offsets). The 8
+// slice groups are then summed by xor shuffles in a fixed order, and each 16-lane
+// group gathers entries e and 16 + e for the coefficient step (all four groups
+// hold the same token; the first stores).
+constexpr int kFinWaveRounds = 16;   // slices per lane: nsplit <= 128
+
+__global__ __launch_bounds__(kFinBlock) void finalize_wave_kernel(FinalizeArgs f) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * (kFinBlock / 64) + uniform(threadIdx.x >> 6);
+    const bool ok = t < f.n;
+    const int64_t tt = ok ? t : 0;
+    const int g = lane >> 3, q = lane & 7;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(f.part, (int64_t)f.nsplit * f.n * kPart * (int64_t)sizeof(float));
+    float4 v[kFinWaveRounds];
+#pragma unroll
+    for (int k = 0; k < kFinWaveRounds; ++k) {
+        const int64_t s = g + 8 * k;
+        const uint32_t off = s < f.nsplit ? (uint32_t)(((s * f.n + tt) * kPart + 4 * q) * sizeof(float)) : kOffMasked;
+        v[k] = buf_load16f(r, off, 0);
+    }
+    float4 acc = v[0];
+#pragma unroll
+    for (int k = 1; k < kFinWaveRounds; ++k) {
+        acc.x += v[k].x; acc.y += v[k].y; acc.z += v[k].z; acc.w += v[k].w;
+    }
+#pragma unroll
+    for (int m = 8; m <= 32; m <<= 1) {
+        acc.x += __shfl_xor(acc.x, m); acc.y += __shfl_xor(acc.y, m);
+        acc.z += __shfl_xor(acc.z, m); acc.w += __shfl_xor(acc.w, m);
+    }
+    // entry e sits in component e % 4 of lane e / 4; entry 16 + e in lane 4 + e / 4
+    const int e = lane & 15, c = e & 3;
+    const float4 p0 = make_float4(__shfl(acc.x, e >> 2), __shfl(acc.y, e >> 2), __shfl(acc.z, e >> 2),
+                                  __shfl(acc.w, e >> 2));
+    const float4 p1 = make_float4(__shfl(acc.x, 4 + (e >> 2)), __shfl(acc.y, 4 + (e >> 2)),
+                                  __shfl(acc.z, 4 + (e >> 2)), __shfl(acc.w, 4 + (e >> 2)));
+    const float a0 = c == 0 ? p0.x : c == 1 ? p0.y : c == 2 ? p0.z : p0.w;
+    const float a1 = c == 0 ? p1.x : c == 1 ? p1.y : c == 2 ? p1.z : p1.w;
+    finalize_coeffs(f, t, e, a0, a1, ok && lane < 16);
 }
 
 // ------------------------------------------------- bf16 projection weights
@@ -1275,7 +1327,7 @@ PassPlan plan_pass(int64_t n, int64_t d, bool bf16) {
     int64_t ns = ceil_div(target_groups, p.tiles > 0 ? p.tiles : 1);
     if (ns < 1) ns = 1;
     if (ns > nunits) ns = nunits;
-    if (ns > 64) ns = 64;
+    if (ns > 8 * kFinWaveRounds) ns = 8 * kFinWaveRounds;   // what the wave finalize reduces
     p.chunks_per_split = (int)ceil_div(nunits, ns) * (unit / kChunk);
     p.nsplit = (int)ceil_div(p.nchunks, p.chunks_per_split);
     // partial rows: nsplit x n x 32 floats
@@ -1411,7 +1463,12 @@ hipError_t launch_pass_and_finalize(const PassRequest& r, hipStream_t stream) {
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)ceil_div(r.n * 16, kFinBlock)), dim3(kFinBlock), 0, stream, f);
+    if (p.nsplit > 8)   // many slices: a wave per token keeps every partial load in flight
+        hipLaunchKernelGGL(finalize_wave_kernel, dim3((unsigned)ceil_div(r.n, kFinBlock / 64)), dim3(kFinBlock), 0,
+                           stream, f);
+    else
+        hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)ceil_div(r.n * 16, kFinBlock)), dim3(kFinBlock), 0,
+                           stream, f);
     return hipGetLastError();
 }
 

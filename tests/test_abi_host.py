@@ -57,7 +57,7 @@ def test_version_and_status_strings():
 
 def test_workspace_size_rule():
     # one 128-byte partial row per (channel slice, token); slices are whole 64-
-    # (bf16) or 128-channel (fp32) steps, at most 64 of them
+    # (bf16) or 128-channel (fp32) steps, at most 128 of them
     assert hc.workspace_size(0, 4, 5120) == 0
     assert hc.workspace_size(16, 3, 5120) == 0
     assert hc.workspace_size(16, 4, 12) == 0
@@ -65,7 +65,7 @@ def test_workspace_size_rule():
         ws = hc.workspace_size(n, 4, d)
         assert ws > 0 and ws % (128 * n) == 0
         nsplit = ws // (128 * n)
-        assert 1 <= nsplit <= min(64, -(-d // 64))
+        assert 1 <= nsplit <= min(128, -(-d // 64))
 
 
 def _split(mixes=A, scale=B, base=C, n=16, hc_=4, iters=20, eps=1e-6, pre=A + 4096, post=A + 8192,
