@@ -1,7 +1,8 @@
 """The oracle's pins must catch plausible mistakes (no GPU).
 
 Each case below plants one mistake in a COPY of the oracle's C source, builds it
-into a temporary library and runs the pin suite against it; the suite must fail.
+into a temporary library and runs the pin suites (four streams and other stream
+counts) against it; the suites must fail.
 Nothing here touches the HIP library.
 """
 import os
@@ -49,6 +50,11 @@ MUTANTS = {
     "e4m3 subnormal step 2^-10": ("nearbyint(ldexp(a, 9))", "nearbyint(ldexp(a, 10))"),
     "e4m3 sign dropped": ("signbit(v) ? 0x80 : 0x00", "0x00"),
     "e4m3 exponent bias 8": ("(((exp + 7) << 3)", "(((exp + 8) << 3)"),
+    # mistakes invisible at four streams
+    "comb offset fixed at 8": ("int i = 2 * hc + j * hc + k;", "int i = 8 + j * hc + k;"),
+    "post offset fixed at 4": ("sigmoid(s1 * m[hc + j] + hc_base[hc + j])", "sigmoid(s1 * m[4 + j] + hc_base[4 + j])"),
+    "column sums over 4 rows": ("        for (int j = 0; j < hc; ++j)\n            s += C[j * hc + k];",
+                                "        for (int j = 0; j < hc && j < 4; ++j)\n            s += C[j * hc + k];"),
 }
 
 
@@ -62,6 +68,7 @@ def test_pins_catch_planted_mistake(name, tmp_path):
     lib = oracle.build(src=str(src), out=str(tmp_path / "libmutant.so"), werror=False)
     env = dict(os.environ, HC_ORACLE_LIB=lib)
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_generic_hc.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, f"pins did not catch mutant '{name}':\n{r.stdout[-2000:]}"
