@@ -6,8 +6,9 @@ tensors) and the current HIP stream. There is no fallback: if the library is not
 built, every call raises.
 
 The functions carry the names of the C entry points. Shapes follow the pages'
-``Block`` methods: streams [..., 4, d], sublayer input/output [..., d], mixes
-[..., 24], pre/post [..., 4], comb [..., 4, 4].
+``Block`` methods: streams [..., hc, d], sublayer input/output [..., d], mixes
+[..., (2+hc)hc], pre/post [..., hc], comb [..., hc, hc]; hc = 4 in the released
+configuration, 1..8 supported.
 """
 from __future__ import annotations
 
@@ -117,7 +118,7 @@ def _workspace(n, hc, d, device, workspace):
 
 
 def hc_mixes(x, hc_fn, norm_eps=NORM_EPS, out=None, workspace=None):
-    """x [..., hc, d] -> mixes [..., 24] fp32 (projection scaled by the RMS statistic)."""
+    """x [..., hc, d] -> mixes [..., (2+hc)hc] fp32 (projection scaled by the RMS statistic)."""
     _dev(x, "x")
     _dev(hc_fn, "hc_fn", torch.float32)
     lead, n, hc, d = _streams_shape(x)
@@ -132,7 +133,8 @@ def hc_mixes(x, hc_fn, norm_eps=NORM_EPS, out=None, workspace=None):
 
 def hc_split_sinkhorn(mixes, hc_scale, hc_base, hc_mult=HC_MULT, sinkhorn_iters=SINKHORN_ITERS,
                       eps=HC_EPS, out=None):
-    """mixes [..., 24] -> (pre [..., 4], post [..., 4], comb [..., 4, 4]), fp32."""
+    """mixes [..., (2+hc)hc] -> (pre [..., hc], post [..., hc], comb [..., hc, hc]), fp32,
+    hc = hc_mult."""
     _dev(mixes, "mixes", torch.float32)
     _dev(hc_scale, "hc_scale", torch.float32)
     _dev(hc_base, "hc_base", torch.float32)

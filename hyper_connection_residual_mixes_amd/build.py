@@ -9,7 +9,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_PATH = os.path.join(PKG, "libhc.so")
-SOURCES = [os.path.join(CSRC, "hc_kernels.hip"), os.path.join(CSRC, "hc_abi.cpp")]
+SOURCES = [os.path.join(CSRC, "hc_kernels.hip"), os.path.join(CSRC, "hc_generic.hip"),
+           os.path.join(CSRC, "hc_abi.cpp")]
 
 # Packed-FP32 VALU forms are switched off for all device code.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -12,7 +12,6 @@
 namespace {
 
 constexpr int kHC = 4;
-constexpr int kMix = 24;
 
 struct Span {
     const void* p;
@@ -35,10 +34,18 @@ int check_shape(int64_t n, int hc, int64_t d, int dtype) {
     // d <= 2^20 keeps every per-wave byte offset of the kernels within 31 bits
     if (n < 0 || d < 1 || d > (int64_t(1) << 20)) return HC_ERR_SHAPE;
     if (dtype != HC_F32 && dtype != HC_BF16) return HC_ERR_UNSUPPORTED;
-    if (hc != kHC || d % 8 != 0) return HC_ERR_UNSUPPORTED;
+    if (hc < 1 || hc > hc::kMaxHC || d % 8 != 0) return HC_ERR_UNSUPPORTED;
     // every byte offset must fit comfortably in 63 bits
     if (n > 0 && (uint64_t)d > (uint64_t(1) << 40) / (uint64_t)n) return HC_ERR_SHAPE;
     return HC_OK;
+}
+
+size_t mix_count(int hc) { return (size_t)(2 + hc) * (size_t)hc; }
+
+// Workspace of the projection for (n, hc, d): the single-pass plan for four
+// streams, the unfused plan otherwise.
+size_t ws_bytes(int64_t n, int hc, int64_t d) {
+    return hc == kHC ? hc::workspace_bytes(n, d) : hc::generic_workspace_bytes(n, hc, d);
 }
 
 int check_eps(float v) { return (std::isfinite(v) && v >= 0.f) ? HC_OK : HC_ERR_ARG; }
@@ -76,7 +83,7 @@ const char* hc_status_string(int status) {
         case HC_OK: return "ok";
         case HC_ERR_NULL: return "a required pointer is NULL";
         case HC_ERR_SHAPE: return "invalid shape (n < 0, d < 1 or too large)";
-        case HC_ERR_UNSUPPORTED: return "unsupported configuration (hc must be 4, d a multiple of 8, dtype fp32 or bf16)";
+        case HC_ERR_UNSUPPORTED: return "unsupported configuration (hc must be 1..8, d a multiple of 8, dtype fp32 or bf16)";
         case HC_ERR_ALIGN: return "misaligned pointer (16 bytes required)";
         case HC_ERR_ARG: return "invalid argument (sinkhorn_iters < 1, or eps/norm_eps negative or not finite)";
         case HC_ERR_ALIAS: return "an output overlaps an input or another output";
@@ -88,25 +95,28 @@ const char* hc_status_string(int status) {
 
 size_t hc_workspace_size(int64_t n, int hc, int64_t d) {
     if (n <= 0 || check_shape(n, hc, d, HC_F32) != HC_OK) return 0;
-    return hc::workspace_bytes(n, d);
+    return ws_bytes(n, hc, d);
 }
 
 int hc_split_sinkhorn(const float* mixes, const float* hc_scale, const float* hc_base, int64_t n, int hc,
                       int sinkhorn_iters, float eps, float* pre, float* post, float* comb, void* stream) {
     if (n < 0) return HC_ERR_SHAPE;
-    if (hc != kHC) return HC_ERR_UNSUPPORTED;
+    if (hc < 1 || hc > hc::kMaxHC) return HC_ERR_UNSUPPORTED;
     if (sinkhorn_iters < 1 || check_eps(eps) != HC_OK) return HC_ERR_ARG;
     if (n == 0) return HC_OK;
     if (!mixes || !hc_scale || !hc_base || !pre || !post || !comb) return HC_ERR_NULL;
     if (!aligned(mixes, 16) || !aligned(pre, 16) || !aligned(post, 16) || !aligned(comb, 16) ||
         !aligned(hc_scale, 4) || !aligned(hc_base, 4))
         return HC_ERR_ALIGN;
-    const size_t un = (size_t)n;
-    const Span outs[] = {{pre, un * 16}, {post, un * 16}, {comb, un * 64}};
-    const Span ins[] = {{mixes, un * kMix * 4}, {hc_scale, 12}, {hc_base, kMix * 4}};
+    const size_t un = (size_t)n, uh = (size_t)hc, M = mix_count(hc);
+    const Span outs[] = {{pre, un * uh * 4}, {post, un * uh * 4}, {comb, un * uh * uh * 4}};
+    const Span ins[] = {{mixes, un * M * 4}, {hc_scale, 12}, {hc_base, M * 4}};
     if (int rc = check_aliases(outs, 3, ins, 3, nullptr, 0)) return rc;
-    return hip_status(hc::launch_split(mixes, hc_scale, hc_base, n, sinkhorn_iters, eps, pre, post, comb,
-                                       static_cast<hipStream_t>(stream)));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hc != kHC)
+        return hip_status(hc::launch_split_generic(mixes, hc_scale, hc_base, n, hc, sinkhorn_iters, eps, pre, post,
+                                                   comb, s));
+    return hip_status(hc::launch_split(mixes, hc_scale, hc_base, n, sinkhorn_iters, eps, pre, post, comb, s));
 }
 
 int hc_pre(const void* x, int dtype, const float* pre_mix, int64_t n, int hc, int64_t d, void* y,
@@ -116,10 +126,13 @@ int hc_pre(const void* x, int dtype, const float* pre_mix, int64_t n, int hc, in
     if (!x || !pre_mix || !y) return HC_ERR_NULL;
     if (!aligned(x, 16) || !aligned(pre_mix, 16) || !aligned(y, 16)) return HC_ERR_ALIGN;
     const size_t es = elem_size(dtype), un = (size_t)n, ud = (size_t)d;
+    const size_t uh = (size_t)hc;
     const Span outs[] = {{y, un * ud * es}};
-    const Span ins[] = {{x, un * kHC * ud * es}, {pre_mix, un * 16}};
+    const Span ins[] = {{x, un * uh * ud * es}, {pre_mix, un * uh * 4}};
     if (int rc = check_aliases(outs, 1, ins, 2, nullptr, 0)) return rc;
-    return hip_status(hc::launch_pre(x, dtype == HC_BF16, pre_mix, n, d, y, static_cast<hipStream_t>(stream)));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hc != kHC) return hip_status(hc::launch_pre_generic(x, dtype == HC_BF16, pre_mix, n, hc, d, y, s));
+    return hip_status(hc::launch_pre(x, dtype == HC_BF16, pre_mix, n, d, y, s));
 }
 
 int hc_rmsnorm_mxfp8(const void* x, int dtype, const float* gain, int64_t n, int64_t d, float norm_eps,
@@ -156,13 +169,16 @@ int hc_post(const void* f, const void* residual, int dtype, const float* post, c
         !aligned(out, 16))
         return HC_ERR_ALIGN;
     const size_t es = elem_size(dtype), un = (size_t)n, ud = (size_t)d;
-    const Span res_span{residual, un * kHC * ud * es};
-    const Span outs[] = {{out, un * kHC * ud * es}};
-    const Span ins[] = {{f, un * ud * es}, res_span, {post, un * 16}, {comb, un * 64}};
+    const size_t uh = (size_t)hc;
+    const Span res_span{residual, un * uh * ud * es};
+    const Span outs[] = {{out, un * uh * ud * es}};
+    const Span ins[] = {{f, un * ud * es}, res_span, {post, un * uh * 4}, {comb, un * uh * uh * 4}};
     const Span allowed[] = {outs[0], res_span};
     if (int rc = check_aliases(outs, 1, ins, 4, allowed, 1)) return rc;
-    return hip_status(hc::launch_post(f, residual, dtype == HC_BF16, post, comb, n, d, out,
-                                      static_cast<hipStream_t>(stream)));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hc != kHC)
+        return hip_status(hc::launch_post_generic(f, residual, dtype == HC_BF16, post, comb, n, hc, d, out, s));
+    return hip_status(hc::launch_post(f, residual, dtype == HC_BF16, post, comb, n, d, out, s));
 }
 
 int hc_mixes(const void* x, int dtype, int64_t n, int hc, int64_t d, const float* hc_fn, float norm_eps,
@@ -172,13 +188,16 @@ int hc_mixes(const void* x, int dtype, int64_t n, int hc, int64_t d, const float
     if (n == 0) return HC_OK;
     if (!x || !hc_fn || !mixes) return HC_ERR_NULL;
     if (!aligned(x, 16) || !aligned(hc_fn, 16) || !aligned(mixes, 16)) return HC_ERR_ALIGN;
-    const size_t ws_need = hc::workspace_bytes(n, d);
+    const size_t ws_need = ws_bytes(n, hc, d);
     if (!workspace || workspace_bytes < ws_need) return HC_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return HC_ERR_ALIGN;
-    const size_t es = elem_size(dtype), un = (size_t)n, ud = (size_t)d;
-    const Span outs[] = {{mixes, un * kMix * 4}, {workspace, ws_need}};
-    const Span ins[] = {{x, un * kHC * ud * es}, {hc_fn, (size_t)kMix * kHC * ud * 4}};
+    const size_t es = elem_size(dtype), un = (size_t)n, ud = (size_t)d, uh = (size_t)hc, M = mix_count(hc);
+    const Span outs[] = {{mixes, un * M * 4}, {workspace, ws_need}};
+    const Span ins[] = {{x, un * uh * ud * es}, {hc_fn, M * uh * ud * 4}};
     if (int rc = check_aliases(outs, 2, ins, 2, nullptr, 0)) return rc;
+    if (hc != kHC)
+        return hip_status(hc::launch_mixes_generic(x, dtype == HC_BF16, n, hc, d, hc_fn, norm_eps, mixes, workspace,
+                                                   static_cast<hipStream_t>(stream)));
     hc::PassRequest r{};
     r.res = x;
     r.hc_fn = hc_fn;
@@ -205,7 +224,7 @@ int hc_fused_step(const void* residual, const void* f_prev, const float* post_pr
     const bool expand = f_prev != nullptr;
     if (expand && (!post_prev || !comb_prev || !streams_out)) return HC_ERR_NULL;
     if (y && !pre_mix) return HC_ERR_NULL;
-    const size_t ws_need = hc::workspace_bytes(n, d);
+    const size_t ws_need = ws_bytes(n, hc, d);
     if (!workspace || workspace_bytes < ws_need) return HC_ERR_WORKSPACE;
     const void* a16[] = {residual, hc_fn, pre, post, comb, workspace};
     for (const void* p : a16)
@@ -215,26 +234,53 @@ int hc_fused_step(const void* residual, const void* f_prev, const float* post_pr
         if (p && !aligned(p, 16)) return HC_ERR_ALIGN;
     if (!aligned(hc_scale, 4) || !aligned(hc_base, 4)) return HC_ERR_ALIGN;
 
-    const size_t es = elem_size(dtype), un = (size_t)n, ud = (size_t)d;
-    const Span res_span{residual, un * kHC * ud * es};
-    const Span so_span{expand ? streams_out : nullptr, un * kHC * ud * es};
+    const size_t es = elem_size(dtype), un = (size_t)n, ud = (size_t)d, uh = (size_t)hc, M = mix_count(hc);
+    const Span res_span{residual, un * uh * ud * es};
+    const Span so_span{expand ? streams_out : nullptr, un * uh * ud * es};
     const Span outs[] = {so_span,
                          {y, un * ud * es},
-                         {pre, un * 16},
-                         {post, un * 16},
-                         {comb, un * 64},
-                         {mixes, un * kMix * 4},
+                         {pre, un * uh * 4},
+                         {post, un * uh * 4},
+                         {comb, un * uh * uh * 4},
+                         {mixes, un * M * 4},
                          {workspace, ws_need}};
     const Span ins[] = {res_span,
                         {f_prev, un * ud * es},
-                        {expand ? post_prev : nullptr, un * 16},
-                        {expand ? comb_prev : nullptr, un * 64},
-                        {y ? pre_mix : nullptr, un * 16},
-                        {hc_fn, (size_t)kMix * kHC * ud * 4},
+                        {expand ? post_prev : nullptr, un * uh * 4},
+                        {expand ? comb_prev : nullptr, un * uh * uh * 4},
+                        {y ? pre_mix : nullptr, un * uh * 4},
+                        {hc_fn, M * uh * ud * 4},
                         {hc_scale, 12},
-                        {hc_base, kMix * 4}};
+                        {hc_base, M * 4}};
     const Span allowed[] = {so_span, res_span};
     if (int rc = check_aliases(outs, 7, ins, 8, allowed, 1)) return rc;
+
+    if (hc != kHC) {
+        hc::GenericRequest g{};
+        g.res = residual;
+        g.f_prev = f_prev;
+        g.post_prev = post_prev;
+        g.comb_prev = comb_prev;
+        g.pre_mix = pre_mix;
+        g.hc_fn = hc_fn;
+        g.scale = hc_scale;
+        g.base = hc_base;
+        g.streams_out = expand ? streams_out : nullptr;
+        g.y = y;
+        g.mixes = mixes;
+        g.pre = pre;
+        g.post = post;
+        g.comb = comb;
+        g.workspace = workspace;
+        g.n = n;
+        g.hc = hc;
+        g.d = d;
+        g.bf16 = dtype == HC_BF16;
+        g.norm_eps = norm_eps;
+        g.iters = sinkhorn_iters;
+        g.eps = eps;
+        return hip_status(hc::launch_fused_generic(g, static_cast<hipStream_t>(stream)));
+    }
 
     hc::PassRequest r{};
     r.res = residual;

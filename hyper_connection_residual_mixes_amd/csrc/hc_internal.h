@@ -57,4 +57,45 @@ hipError_t launch_pass_and_finalize(const PassRequest& r, hipStream_t stream);
 hipError_t launch_rmsnorm_mxfp8(const void* x, bool bf16, const float* gain, int64_t n, int64_t d, float eps,
                                 void* y_norm, uint8_t* q, uint8_t* scale, hipStream_t stream);
 
+// ------------------------------------------- stream counts other than four
+// Unfused kernels for 1 <= hc <= kMaxHC (hc_generic.hip); four streams use the
+// single-pass kernels above.
+constexpr int kMaxHC = 8;
+
+struct GenericRequest {
+    const void* res;         // [n][hc][d]
+    const void* f_prev;      // [n][d] or null (no expand)
+    const float* post_prev;  // [n][hc]
+    const float* comb_prev;  // [n][hc][hc]
+    const float* pre_mix;    // [n][hc] (used when y != null)
+    const float* hc_fn;      // [(2+hc)hc][hc d]
+    const float* scale;      // [3]
+    const float* base;       // [(2+hc)hc]
+    void* streams_out;       // [n][hc][d] when f_prev != null (may be res)
+    void* y;                 // [n][d] or null
+    float* mixes;            // [n][(2+hc)hc] or null (then kept in the workspace)
+    float* pre;
+    float* post;
+    float* comb;
+    void* workspace;         // >= generic_workspace_bytes(n, hc, d)
+    int64_t n;
+    int hc;
+    int64_t d;
+    bool bf16;
+    float norm_eps;
+    int iters;
+    float eps;
+};
+
+size_t generic_workspace_bytes(int64_t n, int hc, int64_t d);
+hipError_t launch_split_generic(const float* mixes, const float* scale, const float* base, int64_t n, int hc,
+                                int iters, float eps, float* pre, float* post, float* comb, hipStream_t stream);
+hipError_t launch_pre_generic(const void* x, bool bf16, const float* pre_mix, int64_t n, int hc, int64_t d, void* y,
+                              hipStream_t stream);
+hipError_t launch_post_generic(const void* f, const void* res, bool bf16, const float* post, const float* comb,
+                               int64_t n, int hc, int64_t d, void* out, hipStream_t stream);
+hipError_t launch_mixes_generic(const void* x, bool bf16, int64_t n, int hc, int64_t d, const float* hc_fn,
+                                float norm_eps, float* mixes, void* workspace, hipStream_t stream);
+hipError_t launch_fused_generic(const GenericRequest& r, hipStream_t stream);
+
 }  // namespace hc

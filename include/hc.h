@@ -1,9 +1,11 @@
 /*
  * hc.h -- C ABI of libhc.so, the MI355X (gfx950) hyper-connection residual mix.
  *
- * The residual of a DeepSeek-V4.1 block is hc = 4 parallel streams of width d.
- * Each sublayer is bracketed by: a projection of the flattened streams to
- * (2+hc)*hc = 24 mix numbers, a split of those numbers into collapse ("pre"),
+ * The residual of a DeepSeek-V4.1 block is hc = 4 parallel streams of width d
+ * (the released configuration; the page's split kernel and Block are written
+ * for any stream count hc). Each sublayer is bracketed by: a projection of the
+ * flattened streams to M = (2+hc)*hc mix numbers (24 at hc = 4), a split of
+ * those numbers into collapse ("pre"),
  * output ("post") and combine ("comb") coefficients made nearly doubly
  * stochastic by Sinkhorn rounds, a collapse of the streams into the sublayer
  * input, and an expansion of the sublayer output back into the streams.
@@ -23,16 +25,19 @@
  *     never allocates, frees or retains them. Tensors are dense and row-major.
  *     n is the number of tokens (batch * positions, flattened).
  *   - Layouts: streams [n][hc][d]; sublayer input/output [n][d];
- *     hc_fn [24][hc*d] fp32 with flat input index c = j*d + e;
- *     mixes [n][24] fp32 (pre logits | post logits | comb logits, comb row-major);
- *     pre, post [n][hc] fp32; comb [n][hc][hc] fp32 where comb[j][k] weighs OLD
- *     stream j into NEW stream k; hc_scale [3], hc_base [24] fp32.
+ *     hc_fn [M][hc*d] fp32 with flat input index c = j*d + e;
+ *     mixes [n][M] fp32 (pre logits (hc) | post logits (hc) | comb logits
+ *     (hc*hc, row-major)); pre, post [n][hc] fp32; comb [n][hc][hc] fp32 where
+ *     comb[j][k] weighs OLD stream j into NEW stream k; hc_scale [3], hc_base
+ *     [M] fp32. M = (2+hc)*hc.
  *   - dtype selects the stream element type: HC_F32 or HC_BF16. Coefficients
  *     and parameters are always fp32. Arithmetic is fp32; bf16 results are
  *     rounded to nearest, ties to even.
- *   - Supported sizes: hc == 4; 8 <= d <= 1048576 and d % 8 == 0; n >= 0
+ *   - Supported sizes: 1 <= hc <= 8; 8 <= d <= 1048576 and d % 8 == 0; n >= 0
  *     (n == 0 is a no-op returning HC_OK without touching any pointer) and
- *     n * d <= 2^40. Larger d or n * d return HC_ERR_SHAPE.
+ *     n * d <= 2^40. Larger d or n * d return HC_ERR_SHAPE. hc == 4 runs the
+ *     single-pass kernels; other stream counts run one kernel per step (the
+ *     fused boundary as expand, projection, split, collapse in sequence).
  *   - Alignment: every tensor pointer (streams, sublayer input/output, hc_fn,
  *     mixes, pre/post/comb and their _prev / pre_mix inputs, workspace) must be
  *     16-byte aligned; hc_scale and hc_base need 4-byte alignment.
@@ -62,7 +67,7 @@ extern "C" {
 #define HC_OK 0
 #define HC_ERR_NULL (-1)        /* a required pointer is NULL */
 #define HC_ERR_SHAPE (-2)       /* n < 0, d < 1 or d, n * d too large */
-#define HC_ERR_UNSUPPORTED (-3) /* hc != 4, d % 8 != 0, unknown dtype */
+#define HC_ERR_UNSUPPORTED (-3) /* hc outside 1..8, d % 8 != 0, unknown dtype */
 #define HC_ERR_ALIGN (-4)       /* a pointer breaks the alignment rule */
 #define HC_ERR_ARG (-5)         /* sinkhorn_iters < 1, eps or norm_eps negative or not finite */
 #define HC_ERR_ALIAS (-6)       /* outputs overlap inputs or each other */
@@ -87,11 +92,11 @@ size_t hc_workspace_size(int64_t n, int hc, int64_t d);
  * diagram "Mixing Coefficients".
  * For each token the hc streams are flattened to D = hc*d values, and
  *   mixes[t][i] = (sum_c hc_fn[i][c] * x[t][c]) / sqrt(mean_c(x[t][c]^2) + norm_eps)
- * for i < 24. One RMS statistic covers all hc*d values of the token. The
- * released configuration uses norm_eps = 1e-20.
+ * for i < M = (2+hc)*hc. One RMS statistic covers all hc*d values of the token.
+ * The released configuration uses norm_eps = 1e-20.
  *   x     [n][hc][d] dtype      in
- *   hc_fn [24][hc*d] fp32       in
- *   mixes [n][24] fp32          out
+ *   hc_fn [M][hc*d] fp32        in
+ *   mixes [n][M] fp32           out
  */
 int hc_mixes(const void* x, int dtype, int64_t n, int hc, int64_t d, const float* hc_fn,
              float norm_eps, float* mixes, void* workspace, size_t workspace_bytes,
@@ -103,13 +108,13 @@ int hc_mixes(const void* x, int dtype, int64_t n, int hc, int64_t d, const float
  * "Sinkhorn Round".
  * With m = mixes[t], s = hc_scale, b = hc_base:
  *   pre[t][j]  = sigmoid(s[0]*m[j] + b[j]) + eps
- *   post[t][j] = 2 * sigmoid(s[1]*m[4+j] + b[4+j])
- *   comb[t]    = Sinkhorn(L), L[j][k] = s[2]*m[8+4j+k] + b[8+4j+k]:
+ *   post[t][j] = 2 * sigmoid(s[1]*m[hc+j] + b[hc+j])
+ *   comb[t]    = Sinkhorn(L), L[j][k] = s[2]*m[2hc+j*hc+k] + b[2hc+j*hc+k]:
  *     row softmax (max subtracted), + eps on every entry, divide each column by
  *     (column sum + eps); then sinkhorn_iters-1 rounds of: divide each row by
  *     (row sum + eps), divide each column by (column sum + eps).
  * Released configuration: sinkhorn_iters = 20, eps = 1e-6.
- *   mixes [n][24] in; pre [n][4], post [n][4], comb [n][4][4] out (fp32).
+ *   mixes [n][M] in; pre [n][hc], post [n][hc], comb [n][hc][hc] out (fp32).
  */
 int hc_split_sinkhorn(const float* mixes, const float* hc_scale, const float* hc_base,
                       int64_t n, int hc, int sinkhorn_iters, float eps, float* pre,
@@ -169,9 +174,9 @@ int hc_rmsnorm_mxfp8(const void* x, int dtype, const float* gain, int64_t n, int
  *       previous sublayer produced (skipped when y == NULL).
  * mixes may be NULL (not stored). streams_out == residual is allowed.
  *   residual [n][hc][d], f_prev [n][d] dtype; post_prev [n][hc], comb_prev
- *   [n][hc][hc], pre_mix [n][hc], hc_fn [24][hc*d], hc_scale [3], hc_base [24]
+ *   [n][hc][hc], pre_mix [n][hc], hc_fn [M][hc*d], hc_scale [3], hc_base [M]
  *   fp32 in; streams_out [n][hc][d], y [n][d] dtype out; pre, post [n][hc],
- *   comb [n][hc][hc], mixes [n][24] fp32 out.
+ *   comb [n][hc][hc], mixes [n][M] fp32 out.
  */
 int hc_fused_step(const void* residual, const void* f_prev, const float* post_prev,
                   const float* comb_prev, const float* pre_mix, const float* hc_fn,

@@ -59,13 +59,21 @@ def test_workspace_size_rule():
     # one 128-byte partial row per (channel slice, token); slices are whole 64-
     # (bf16) or 128-channel (fp32) steps, at most 128 of them
     assert hc.workspace_size(0, 4, 5120) == 0
-    assert hc.workspace_size(16, 3, 5120) == 0
+    assert hc.workspace_size(16, 9, 5120) == 0
+    assert hc.workspace_size(16, 0, 5120) == 0
     assert hc.workspace_size(16, 4, 12) == 0
     for n, d in ((16, 256), (64, 5120), (4096, 5120), (65536, 5120), (37, 264)):
         ws = hc.workspace_size(n, 4, d)
         assert ws > 0 and ws % (128 * n) == 0
         nsplit = ws // (128 * n)
         assert 1 <= nsplit <= min(128, -(-d // 64))
+    # other stream counts: partial rows of (2+hc)hc dots + 1 sum of squares (padded
+    # to 4 floats) per (slice, token), then n scratch mix rows
+    for hc_, n, d in ((1, 16, 256), (2, 37, 264), (8, 64, 5120), (3, 4096, 5120)):
+        M = (2 + hc_) * hc_
+        pg = (M + 1 + 3) // 4 * 4
+        ws = hc.workspace_size(n, hc_, d)
+        assert ws >= n * pg * 4 + n * M * 4
 
 
 def _split(mixes=A, scale=B, base=C, n=16, hc_=4, iters=20, eps=1e-6, pre=A + 4096, post=A + 8192,
@@ -77,7 +85,8 @@ def _split(mixes=A, scale=B, base=C, n=16, hc_=4, iters=20, eps=1e-6, pre=A + 40
 def test_split_validation():
     assert _split(n=0) == OK            # no-op touches nothing
     assert _split(n=-1) == SHAPE
-    assert _split(hc_=3) == UNSUP
+    assert _split(hc_=9) == UNSUP
+    assert _split(hc_=0) == UNSUP
     assert _split(iters=0) == ARG
     assert _split(eps=-1.0) == ARG
     assert _split(eps=float("nan")) == ARG
@@ -97,7 +106,8 @@ def test_pre_validation():
     assert _pre(d=260) == UNSUP
     assert _pre(d=(1 << 20) + 8) == SHAPE   # beyond the supported width
     assert _pre(dtype=2) == UNSUP
-    assert _pre(hc_=2) == UNSUP
+    assert _pre(hc_=9) == UNSUP
+    assert _pre(hc_=0) == UNSUP
     assert _pre(x=None) == NULL
     assert _pre(y=C + 2) == ALIGN
     assert _pre(y=A + 1024) == ALIAS
