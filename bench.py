@@ -37,14 +37,17 @@ METRIC = "tokens/s and achieved HBM TB/s (% of peak), fused HC mix, d=5120, 4 st
 PEAK_HBM_GBS = 8000.0
 
 
-def algorithmic_bytes(n: int, d: int, es: int = 2):
+def algorithmic_bytes(n: int, d: int, es: int = 2, hc: int = 4):
     """Bytes each entry point must move (read + write), counted once each.
-    Coefficients are fp32: pre/post 16 B, comb 64 B per token; hc_fn 24*4d*4 B plus
-    base (96 B) and scale (12 B) once per call."""
-    w = 24 * 4 * d * 4 + 96 + 12
-    k1 = n * (4 * d * es + 16 + d * es + 96) + w                 # x, pi -> y, pre/post/comb
-    k2 = n * (4 * d * es + d * es + 96 + 4 * d * es + d * es + 96) + w   # + f, post/comb/pi -> x1, y
-    k3 = n * (d * es + 4 * d * es + 80 + 4 * d * es)             # f, x1, post/comb -> x2
+    Coefficients are fp32: pre/post 4*hc B, comb 4*hc^2 B per token (16, 16, 64 at
+    hc = 4); hc_fn M*hc*d*4 B plus base (4M B) and scale (12 B) once per call,
+    M = (2+hc)hc mix numbers."""
+    M = (2 + hc) * hc
+    coef = 4 * M                                                 # pre + post + comb
+    w = M * hc * d * 4 + 4 * M + 12
+    k1 = n * (hc * d * es + 4 * hc + d * es + coef) + w          # x, pi -> y, pre/post/comb
+    k2 = n * (hc * d * es + d * es + coef + hc * d * es + d * es + coef) + w   # + f, post/comb/pi -> x1, y
+    k3 = n * (d * es + hc * d * es + 4 * (hc + hc * hc) + hc * d * es)         # f, x1, post/comb -> x2
     return dict(attn_fused=k1, ffn_fused=k2, ffn_post=k3, block=k1 + k2 + k3)
 
 
@@ -168,6 +171,45 @@ def decode_latency(dev, reps: int = 300):
             "us_per_block_eager": eager_wall * 1e6, "us_per_block_eager_gpu": eager_gpu * 1e6,
             "us_per_block_graph": graph_wall * 1e6, "tokens_per_s_graph": n / graph_wall,
             "algorithmic_bytes": block_bytes, "achieved_gb_s_graph": block_bytes / graph_wall / 1e9}
+
+
+def generic_hc_blocks(dev, steps: int = 10):
+    """The prefill block (4096 tokens x hc streams x 5120 bf16) at stream counts
+    other than four, which run one kernel per step; timed with HIP events around
+    `steps` blocks after a warm-up."""
+    import torch
+    import hc_inputs
+    import hyper_connection_residual_mixes_amd as hc
+    out = {}
+    for hc_ in (2, 8):
+        w = hc_inputs.Workload(f"prefill_hc{hc_}", 1, 4096, 5120, torch.bfloat16, hc=hc_)
+        inp = hc_inputs.block_inputs(w, seed=0, device=dev, outlier_frac=0.01)
+        n, d = w.n, w.d
+        pi, _, _ = hc.hc_split_sinkhorn(*inp["prev"], hc_mult=hc_)
+        ws = torch.empty(hc.workspace_size(n, hc_, d), dtype=torch.uint8, device=dev)
+        x1 = torch.empty_like(inp["x"])
+        x2 = torch.empty_like(inp["x"])
+
+        def step():
+            hc.block(inp["x"], pi, inp["attn"], inp["ffn"], inp["f_attn"], inp["f_ffn"], x1_out=x1, x2_out=x2,
+                     workspace=ws)
+
+        for _ in range(2):
+            step()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) * 1e-3 / steps
+        ab = algorithmic_bytes(n, d, hc=hc_)["block"]
+        out[f"hc{hc_}"] = {"workload": f"prefill block, {n} tokens x {hc_} streams x {d} bf16",
+                           "us_per_block": sec * 1e6, "tokens_per_s": n / sec, "algorithmic_bytes": ab,
+                           "effective_gb_s": ab / sec / 1e9, "frac": ab / sec / 1e9 / PEAK_HBM_GBS}
+        del inp, x1, x2, ws
+    return out
 
 
 def main():
@@ -302,6 +344,7 @@ def main():
                                      "traffic": stored_traffic(k)} for k in per},
     }
     next_rows["decode"] = decode_latency(dev)
+    next_rows["generic_hc"] = generic_hc_blocks(dev)
     result["next_rows"] = next_rows
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on every input set", file=sys.stderr, flush=True)

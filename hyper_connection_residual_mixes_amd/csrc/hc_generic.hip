@@ -12,11 +12,13 @@
 // a kernel of its own; the fused boundary is their composition:
 //   split_generic_kernel    a wave per token; lane j*hc + k owns comb[j][k], rows
 //                           and columns are summed with cross-lane reads.
-//   pre_generic_kernel      collapse, one lane per (token, 8 channels).
-//   post_generic_kernel     expand + combine, one lane per (token, 8 channels).
-//   mixes_partial_kernel    16 tokens x one slice of the flattened hc*d axis per
-//                           workgroup: the (2+hc)*hc partial dot products and the
-//                           partial sum of squares, from LDS tiles of 64 columns.
+//   pre_generic_kernel      collapse, one lane per (token, 8 channels), a wave
+//                           per token and 512 channels.
+//   post_generic_kernel     expand + combine, the same mapping.
+//   mixes_partial_kernel    64 tokens x one slice of the flattened hc*d axis per
+//                           workgroup: the (2+hc)*hc partial dot products (fp32
+//                           MFMA) and the partial sum of squares, from LDS tiles
+//                           of 64 columns.
 //   mixes_finalize_kernel   a wave per token: partial rows summed over the slices
 //                           in order, scaled by the RMS statistic.
 //
@@ -34,7 +36,7 @@ typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kGBlock = 256;
-constexpr int kGTok = 16;       // tokens per projection workgroup
+constexpr int kGTok = 64;       // tokens per projection workgroup (16 per wave)
 constexpr int kGCols = 64;      // flattened columns per LDS tile
 constexpr int kGMaxSplit = 64;  // slices of the flattened axis
 
@@ -125,15 +127,26 @@ __global__ __launch_bounds__(kGBlock) void split_generic_kernel(const float* __r
 }
 
 // --------------------------------------------------------- collapse / expand
+// A wave covers one token and 64 of its 8-channel chunks (wave (t, wc) of the
+// grid owns chunks wc*64 + lane), so the token's coefficients are wave-uniform
+// and read once per wave through the scalar cache.
+__device__ __forceinline__ bool wave_token(int64_t n, int64_t per_tok, int64_t& t, int64_t& e) {
+    const int64_t wpt = (per_tok + 63) >> 6;   // waves per token
+    const int64_t gw = (int64_t)blockIdx.x * (kGBlock / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    t = gw / wpt;
+    const int64_t c = (gw - t * wpt) * 64 + (threadIdx.x & 63);
+    e = c << 3;
+    return t < n && c < per_tok;
+}
+
+int64_t wave_grid(int64_t n, int64_t d) { return (n * (((d >> 3) + 63) >> 6) + kGBlock / 64 - 1) / (kGBlock / 64); }
+
 template <bool kBf16>
 __global__ __launch_bounds__(kGBlock) void pre_generic_kernel(const void* __restrict__ x,
                                                               const float* __restrict__ pre_mix, int64_t n,
                                                               int hc, int64_t d, void* __restrict__ y) {
-    const int64_t per_tok = d >> 3;
-    const int64_t gid = (int64_t)blockIdx.x * kGBlock + threadIdx.x;
-    if (gid >= n * per_tok) return;
-    const int64_t t = gid / per_tok;
-    const int64_t e = (gid - t * per_tok) << 3;
+    int64_t t, e;
+    if (!wave_token(n, d >> 3, t, e)) return;
     float acc[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[c] = 0.f;
@@ -154,11 +167,8 @@ __global__ __launch_bounds__(kGBlock) void post_generic_kernel(const void* __res
                                                                const float* __restrict__ post,
                                                                const float* __restrict__ comb, int64_t n, int hc,
                                                                int64_t d, void* out) {
-    const int64_t per_tok = d >> 3;
-    const int64_t gid = (int64_t)blockIdx.x * kGBlock + threadIdx.x;
-    if (gid >= n * per_tok) return;
-    const int64_t t = gid / per_tok;
-    const int64_t e = (gid - t * per_tok) << 3;
+    int64_t t, e;
+    if (!wave_token(n, d >> 3, t, e)) return;
     float fv[8], rv[kMaxHC][8];
     load8<kBf16>(f, t * d + e, fv);
 #pragma unroll
@@ -183,19 +193,92 @@ __global__ __launch_bounds__(kGBlock) void post_generic_kernel(const void* __res
 }
 
 // ------------------------------------------------------------- projection
-// Workgroup (tile, slice): tokens tile*16 .. +16 and flattened columns
-// [slice * cols_per_split, +cols_per_split). Lane (tok = tid % 16, g = tid / 16)
-// accumulates mix rows g, g + 16, ... (R of them) for its token, and every lane
-// the token's sum of squares (the g == 0 lanes store it). Tiles of 64 columns of
-// the streams and of hc_fn are staged in LDS (rows padded by one float); rows of
-// the hc_fn tile past the last mix stay zero.
+// Workgroup (tile, slice): tokens tile*64 .. +64 and flattened columns
+// [slice * cols_per_split, +cols_per_split), walked in tiles of 64 columns
+// staged in LDS (streams converted to fp32, and the hc_fn rows; rows of the hc_fn
+// tile past the last mix are zero). The next tile is fetched into registers
+// while the current one is multiplied. Wave w multiplies its 16 tokens by the R
+// 16-wide column tiles of hc_fn with v_mfma_f32_16x16x4f32 (exact fp32 products,
+// fp32 accumulation): lane l (row l % 16, group g = l / 16) feeds, at each of the
+// 16 MFMA steps of a 64-column tile, column 16 g + step to both operands, so its
+// operands are 128-bit LDS reads of 4 consecutive columns. The sum of squares is
+// accumulated by the same lanes on the VALU and summed over the 4 groups at the
+// end. Output: one partial row per (slice, token): the (2+hc)hc dots, then the
+// sum of squares.
+constexpr int kGRow = kGCols + 4;   // LDS row stride (floats)
+
+typedef float floatx4_g __attribute__((ext_vector_type(4)));
+
+// One 64-column tile as fetched from memory, held in registers until it is
+// written to LDS: lane tid owns stream columns (tid % 4) * 16 .. +16 of token
+// tid / 4 (raw words), and float4 slots tid + 256 r of the hc_fn tile (16 slots
+// per row, rows past the last mix read as zero).
+template <bool kBf16, int R>
+struct GenericStage {
+    uint4 xw[kBf16 ? 2 : 4];
+    float4 wv[R];
+};
+
+template <bool kBf16, int R>
+__device__ __forceinline__ void stage_load(GenericStage<kBf16, R>& st, const void* x, const float* hc_fn, int64_t n,
+                                           int M, int64_t K, int64_t t0, int64_t c0, int64_t c_end) {
+    const int tid = threadIdx.x, row = tid >> 2, col = (tid & 3) * 16;
+    const int64_t t = t0 + row;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {   // two halves of 8 columns; K and the slice bounds are multiples of 8
+        const int64_t c = c0 + col + 8 * h;
+        const bool ok = t < n && c < c_end;
+        if constexpr (kBf16) {
+            st.xw[h] = ok ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + t * K + c)
+                          : make_uint4(0, 0, 0, 0);
+        } else {
+            const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(x) + t * K + c);
+            st.xw[2 * h] = ok ? p[0] : make_uint4(0, 0, 0, 0);
+            st.xw[2 * h + 1] = ok ? p[1] : make_uint4(0, 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int q = tid + kGBlock * r, i = q / (kGCols / 4), lc = (q % (kGCols / 4)) * 4;
+        const int64_t c = c0 + lc;
+        st.wv[r] = (i < M && c < c_end) ? *reinterpret_cast<const float4*>(hc_fn + (int64_t)i * K + c)
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+}
+
+template <bool kBf16, int R>
+__device__ __forceinline__ void stage_store(const GenericStage<kBf16, R>& st, float* xs, float* ws) {
+    const int tid = threadIdx.x, row = tid >> 2, col = (tid & 3) * 16;
+    float4* dst = reinterpret_cast<float4*>(xs + row * kGRow + col);
+    if constexpr (kBf16) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t u[4] = {st.xw[h].x, st.xw[h].y, st.xw[h].z, st.xw[h].w};
+            dst[2 * h] = make_float4(__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u),
+                                     __uint_as_float(u[1] << 16), __uint_as_float(u[1] & 0xffff0000u));
+            dst[2 * h + 1] = make_float4(__uint_as_float(u[2] << 16), __uint_as_float(u[2] & 0xffff0000u),
+                                         __uint_as_float(u[3] << 16), __uint_as_float(u[3] & 0xffff0000u));
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            dst[i] = make_float4(__uint_as_float(st.xw[i].x), __uint_as_float(st.xw[i].y),
+                                 __uint_as_float(st.xw[i].z), __uint_as_float(st.xw[i].w));
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int q = tid + kGBlock * r, i = q / (kGCols / 4), lc = (q % (kGCols / 4)) * 4;
+        *reinterpret_cast<float4*>(ws + i * kGRow + lc) = st.wv[r];
+    }
+}
+
 template <bool kBf16, int R>
 __global__ __launch_bounds__(kGBlock) void mixes_partial_kernel(const void* __restrict__ x,
                                                                 const float* __restrict__ hc_fn, int64_t n,
                                                                 int hc, int64_t d, int cols_per_split,
                                                                 int nsplit, float* __restrict__ part, int pg) {
-    __shared__ float xs[kGTok][kGCols + 1];
-    __shared__ float ws[16 * R][kGCols + 1];
+    __shared__ __attribute__((aligned(16))) float xs[kGTok * kGRow];
+    __shared__ __attribute__((aligned(16))) float ws[16 * R * kGRow];
     const int M = (2 + hc) * hc;
     const int64_t K = (int64_t)hc * d;
     const int64_t tile = blockIdx.x / nsplit;
@@ -203,55 +286,54 @@ __global__ __launch_bounds__(kGBlock) void mixes_partial_kernel(const void* __re
     const int64_t t0 = tile * kGTok;
     const int64_t c_begin = (int64_t)slice * cols_per_split;
     const int64_t c_end = c_begin + cols_per_split < K ? c_begin + cols_per_split : K;
-    const int tid = threadIdx.x, tok = tid % kGTok, g = tid / kGTok;
-    for (int q = tid; q < 16 * R * (kGCols + 1); q += kGBlock) (&ws[0][0])[q] = 0.f;
-    float acc[R], ss = 0.f;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r16 = lane & 15, g = lane >> 4;
+    floatx4_g acc[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+    for (int r = 0; r < R; ++r) acc[r] = floatx4_g{0.f, 0.f, 0.f, 0.f};
+    float ss = 0.f;
+    GenericStage<kBf16, R> st;
+    stage_load<kBf16, R>(st, x, hc_fn, n, M, K, t0, c_begin, c_end);
     for (int64_t c0 = c_begin; c0 < c_end; c0 += kGCols) {
-        __syncthreads();   // the previous tile is consumed (and the zero fill is done)
-        {   // streams: 16 tokens x 64 columns, 4 consecutive columns per lane
-            const int lt = tid / 16, lc = (tid % 16) * 4;
-            const int64_t t = t0 + lt, c = c0 + lc;
-            float v[4] = {0.f, 0.f, 0.f, 0.f};
-            if (t < n && c < c_end) {   // K is a multiple of 8: the 4 columns are all in or all out
-                if constexpr (kBf16) {
-                    const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(x) + t * K + c);
-                    v[0] = __uint_as_float(w.x << 16);
-                    v[1] = __uint_as_float(w.x & 0xffff0000u);
-                    v[2] = __uint_as_float(w.y << 16);
-                    v[3] = __uint_as_float(w.y & 0xffff0000u);
-                } else {
-                    const float4 w = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + t * K + c);
-                    v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+        __syncthreads();   // the previous tile is consumed
+        stage_store<kBf16, R>(st, xs, ws);
+        __syncthreads();
+        if (c0 + kGCols < c_end)   // the next tile's loads run under this tile's MFMAs
+            stage_load<kBf16, R>(st, x, hc_fn, n, M, K, t0, c0 + kGCols, c_end);
+        const float* xa = xs + (w * 16 + r16) * kGRow + 16 * g;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 a = *reinterpret_cast<const float4*>(xa + 4 * q4);
+            float4 b[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                b[r] = *reinterpret_cast<const float4*>(ws + (r * 16 + r16) * kGRow + 16 * g + 4 * q4);
+            const float av[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ss = fmaf(av[e], av[e], ss);
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const float bv[4] = {b[r].x, b[r].y, b[r].z, b[r].w};
+                    acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bv[e], acc[r], 0, 0, 0);
                 }
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) xs[lt][lc + i] = v[i];
-        }
-        for (int q = tid; q < M * (kGCols / 4); q += kGBlock) {   // hc_fn: M rows x 64 columns
-            const int i = q / (kGCols / 4), lc = (q % (kGCols / 4)) * 4;
-            const int64_t c = c0 + lc;
-            float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (c < c_end) w = *reinterpret_cast<const float4*>(hc_fn + (int64_t)i * K + c);
-            ws[i][lc] = w.x; ws[i][lc + 1] = w.y; ws[i][lc + 2] = w.z; ws[i][lc + 3] = w.w;
-        }
-        __syncthreads();
-#pragma unroll 8
-        for (int kk = 0; kk < kGCols; ++kk) {
-            const float xv = xs[tok][kk];
-            ss = fmaf(xv, xv, ss);
-#pragma unroll
-            for (int r = 0; r < R; ++r) acc[r] = fmaf(xv, ws[g + 16 * r][kk], acc[r]);
         }
     }
-    const int64_t t = t0 + tok;
-    if (t >= n) return;
-    float* row = part + ((int64_t)slice * n + t) * pg;
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    // accumulator lane l: tokens 4 g + i (i < 4) of the wave's 16, mix r*16 + r16
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-        if (g + 16 * r < M) row[g + 16 * r] = acc[r];
-    if (g == 0) row[M] = ss;
+    for (int r = 0; r < R; ++r) {
+        const int mix = r * 16 + r16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t t = t0 + w * 16 + 4 * g + i;
+            if (t < n && mix < M) part[((int64_t)slice * n + t) * pg + mix] = acc[r][i];
+        }
+    }
+    const int64_t ts = t0 + w * 16 + r16;
+    if (g == 0 && ts < n) part[((int64_t)slice * n + ts) * pg + M] = ss;
 }
 
 // A wave per token: lane l sums entries l and l + 64 of the partial rows over the
@@ -340,7 +422,7 @@ hipError_t launch_split_generic(const float* mixes, const float* scale, const fl
 
 hipError_t launch_pre_generic(const void* x, bool bf16, const float* pre_mix, int64_t n, int hc, int64_t d, void* y,
                               hipStream_t stream) {
-    const dim3 grid((unsigned)ceil_div_g(n * (d / 8), kGBlock));
+    const dim3 grid((unsigned)wave_grid(n, d));
     if (bf16)
         hipLaunchKernelGGL(pre_generic_kernel<true>, grid, dim3(kGBlock), 0, stream, x, pre_mix, n, hc, d, y);
     else
@@ -350,7 +432,7 @@ hipError_t launch_pre_generic(const void* x, bool bf16, const float* pre_mix, in
 
 hipError_t launch_post_generic(const void* f, const void* res, bool bf16, const float* post, const float* comb,
                                int64_t n, int hc, int64_t d, void* out, hipStream_t stream) {
-    const dim3 grid((unsigned)ceil_div_g(n * (d / 8), kGBlock));
+    const dim3 grid((unsigned)wave_grid(n, d));
     if (bf16)
         hipLaunchKernelGGL(post_generic_kernel<true>, grid, dim3(kGBlock), 0, stream, f, res, post, comb, n, hc, d,
                            out);
