@@ -18,8 +18,11 @@
 //   pass_kernel         the same pass for fp32 streams (fp32 MFMA).
 //   finalize_kernel     16 lanes per token: reduce the slice partials in a fixed
 //                       order, scale by the RMS statistic, and (optionally) split.
+//   finalize_wave_kernel the same with a wave per token, for many slices.
 //   rmsnorm_mxfp8_kernel the sublayer RMSNorm (learned gain) of the collapsed
-//                       input and its MXFP8 cast, one workgroup per token row.
+//                       input and its MXFP8 cast, a wave per token row.
+//
+// Stream counts other than four run the kernels of hc_generic.hip.
 //
 // All arithmetic is fp32 (MFMA products exact, fp32 accumulation). bf16 values
 // are rounded to nearest-even (v_cvt_pk_bf16_f32).
