@@ -641,12 +641,29 @@ struct FinalizeArgs {
     float* comb;
 };
 
+// The split parameters lane e of a 16-lane group needs, fetched before the
+// partial rows so that both are in flight together.
+struct CoefParams {
+    float s0, s1, s2, b_e, b_8e;   // hc_scale[0..2], hc_base[e], hc_base[8 + e]
+};
+__device__ __forceinline__ CoefParams load_coef_params(const FinalizeArgs& f, int e) {
+    CoefParams c{};
+    if (f.split) {   // uniform
+        c.s0 = f.scale[0];
+        c.s1 = f.scale[1];
+        c.s2 = f.scale[2];
+        c.b_e = f.base[e];
+        c.b_8e = f.base[8 + e];
+    }
+    return c;
+}
+
 // The coefficients of token t from its reduced partial row: lane e of a 16-lane
 // group holds entries e (a0) and 16 + e (a1). Every lane of the wave must call it
 // (row and column sums are DPP steps within the group); only lanes with `store`
 // write.
-__device__ __forceinline__ void finalize_coeffs(const FinalizeArgs& f, int64_t t, int e, float a0, float a1,
-                                                bool store) {
+__device__ __forceinline__ void finalize_coeffs(const FinalizeArgs& f, const CoefParams& cp, int64_t t, int e,
+                                                float a0, float a1, bool store) {
     const int lane16 = (threadIdx.x & 63) & ~15;
     const float sumsq = __shfl(a1, lane16 + (kMix - 16));
     const float rstd = 1.0f / sqrtf(sumsq / (float)f.D + f.norm_eps);
@@ -661,7 +678,7 @@ __device__ __forceinline__ void finalize_coeffs(const FinalizeArgs& f, int64_t t
     const float lo = __shfl(m0, lane16 + ((8 + e) & 15));
     const float hi = __shfl(m1, lane16 + ((e + 8) & 15));
     const float m = e < 8 ? lo : hi;
-    float c = m * f.scale[2] + f.base[8 + e];
+    float c = m * cp.s2 + cp.b_8e;
     // row softmax (max subtracted), + eps
     float mx = fmaxf(c, dpp<kQuadSwap1>(c));
     mx = fmaxf(mx, dpp<kQuadSwap2>(mx));
@@ -674,24 +691,39 @@ __device__ __forceinline__ void finalize_coeffs(const FinalizeArgs& f, int64_t t
     }
     if (store) {
         f.comb[t * 16 + e] = c;
-        if (e < kHC) f.pre[t * kHC + e] = sigmoid(m0 * f.scale[0] + f.base[e]) + f.eps;
-        else if (e < 2 * kHC) f.post[t * kHC + e - kHC] = 2.0f * sigmoid(m0 * f.scale[1] + f.base[e]);
+        if (e < kHC) f.pre[t * kHC + e] = sigmoid(m0 * cp.s0 + cp.b_e) + f.eps;
+        else if (e < 2 * kHC) f.post[t * kHC + e - kHC] = 2.0f * sigmoid(m0 * cp.s1 + cp.b_e);
     }
 }
 
 // 16 lanes per token: token t (shared by the 16-lane group; t >= n: computes on
 // token 0, stores nothing), lane e of the group reduces entries e and 16 + e over
-// the slices in order. Suits a few slices.
+// the slices in order. Serves up to kFin16Slices slices (more take the wave
+// finalize): every slice's load is issued before the first wait; slices past
+// nsplit re-read the last one and are weighted by zero (v * 0 = 0, v * 1 = v, so
+// the sum is that of the real slices, in order).
+constexpr int kFin16Slices = 8;
+
 __device__ __forceinline__ void finalize16(const FinalizeArgs& f, int64_t t, int e) {
     const bool ok = t < f.n;
     const int64_t tt = ok ? t : 0;
-    float a0 = 0.f, a1 = 0.f;
-    for (int s = 0; s < f.nsplit; ++s) {
-        const float* p = f.part + ((int64_t)s * f.n + tt) * kPart;
-        a0 += p[e];
-        a1 += p[16 + e];                   // entries 16..31; 25..31 are never used below
+    const CoefParams cp = load_coef_params(f, e);
+    float v0[kFin16Slices], v1[kFin16Slices];
+#pragma unroll
+    for (int s = 0; s < kFin16Slices; ++s) {
+        const int sc = s < f.nsplit ? s : f.nsplit - 1;
+        const float* p = f.part + ((int64_t)sc * f.n + tt) * kPart;
+        v0[s] = p[e];
+        v1[s] = p[16 + e];                 // entries 16..31; 25..31 are never used below
     }
-    finalize_coeffs(f, t, e, a0, a1, ok);
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int s = 0; s < kFin16Slices; ++s) {
+        const float m = s < f.nsplit ? 1.f : 0.f;
+        a0 += v0[s] * m;
+        a1 += v1[s] * m;
+    }
+    finalize_coeffs(f, cp, t, e, a0, a1, ok);
 }
 
 constexpr int kFinBlock = 256;
@@ -714,6 +746,7 @@ __global__ __launch_bounds__(kFinBlock) void finalize_wave_kernel(FinalizeArgs f
     const bool ok = t < f.n;
     const int64_t tt = ok ? t : 0;
     const int g = lane >> 3, q = lane & 7;
+    const CoefParams cp = load_coef_params(f, lane & 15);
     const __amdgpu_buffer_rsrc_t r = make_rsrc(f.part, (int64_t)f.nsplit * f.n * kPart * (int64_t)sizeof(float));
     float4 v[kFinWaveRounds];
 #pragma unroll
@@ -740,7 +773,7 @@ __global__ __launch_bounds__(kFinBlock) void finalize_wave_kernel(FinalizeArgs f
                                   __shfl(acc.z, 4 + (e >> 2)), __shfl(acc.w, 4 + (e >> 2)));
     const float a0 = c == 0 ? p0.x : c == 1 ? p0.y : c == 2 ? p0.z : p0.w;
     const float a1 = c == 0 ? p1.x : c == 1 ? p1.y : c == 2 ? p1.z : p1.w;
-    finalize_coeffs(f, t, e, a0, a1, ok && lane < 16);
+    finalize_coeffs(f, cp, t, e, a0, a1, ok && lane < 16);
 }
 
 // ------------------------------------------------- bf16 projection weights
@@ -1466,7 +1499,7 @@ hipError_t launch_pass_and_finalize(const PassRequest& r, hipStream_t stream) {
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    if (p.nsplit > 8)   // many slices: a wave per token keeps every partial load in flight
+    if (p.nsplit > kFin16Slices)   // many slices: a wave per token keeps every partial load in flight
         hipLaunchKernelGGL(finalize_wave_kernel, dim3((unsigned)ceil_div(r.n, kFinBlock / 64)), dim3(kFinBlock), 0,
                            stream, f);
     else
