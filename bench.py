@@ -212,6 +212,55 @@ def generic_hc_blocks(dev, steps: int = 10):
     return out
 
 
+def long_prefill_steady(dev, steps: int = 8):
+    """The long-prefill workload's steady state (2 x 32768 tokens, 4 streams x 5120 bf16):
+    the per-sublayer boundary with expand, coefficients and collapse
+    (hc_fused_step), chained step after step on double-buffered streams, with two
+    parameter sets and two sublayer outputs alternating. A step's working set
+    (~7 GB) is far beyond the caches, so this is the HBM-bound rate."""
+    import torch
+    import hc_inputs
+    import hyper_connection_residual_mixes_amd as hc
+    w = hc_inputs.LONG_PREFILL
+    n, d = w.n, w.d
+    g = hc_inputs.generator(7, dev)
+    params = [hc_inputs.mix_params(g, 4, d, "uniform", dev) for _ in range(2)]
+    cur = hc_inputs.streams(g, n, 4, d, w.dtype, device=dev)
+    nxt = torch.empty_like(cur)
+    fs = [hc_inputs.sublayer_output(g, n, d, w.dtype, dev) for _ in range(2)]
+    y = torch.empty(n, d, dtype=w.dtype, device=dev)
+    ws = torch.empty(hc.workspace_size(n, 4, d), dtype=torch.uint8, device=dev)
+    pi = torch.full((n, 4), 0.25, device=dev)
+    first = hc.hc_fused_step(cur, *params[0], pre_mix=pi, y=y, workspace=ws)
+    coef = (first["pre"], first["post"], first["comb"])
+    outs = [tuple(torch.empty(sh, device=dev) for sh in ((n, 4), (n, 4), (n, 4, 4))) for _ in range(2)]
+
+    def step(i):
+        nonlocal cur, nxt, coef
+        r = hc.hc_fused_step(cur, *params[i % 2], pre_mix=coef[0], f_prev=fs[i % 2], post_prev=coef[1],
+                             comb_prev=coef[2], streams_out=nxt, y=y, out=outs[i % 2], workspace=ws)
+        coef = (r["pre"], r["post"], r["comb"])
+        cur, nxt = nxt, cur
+
+    for i in range(2):
+        step(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / steps
+    ab = algorithmic_bytes(n, d)["ffn_fused"]
+    res = {"workload": f"long-prefill steady state: hc_fused_step with expand + collapse, {n} tokens x 4 x {d} bf16",
+           "us_per_sublayer": sec * 1e6, "tokens_per_s_per_sublayer": n / sec,
+           "us_all_80_sublayers": 80 * sec * 1e6, "algorithmic_bytes": ab,
+           "effective_gb_s": ab / sec / 1e9, "frac": ab / sec / 1e9 / PEAK_HBM_GBS}
+    del cur, nxt, fs, y, ws, params, outs
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -351,6 +400,7 @@ def main():
     }
     next_rows["decode"] = decode_latency(dev)
     next_rows["generic_hc"] = generic_hc_blocks(dev)
+    next_rows["long_prefill"] = long_prefill_steady(dev)
     result["next_rows"] = next_rows
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on every input set", file=sys.stderr, flush=True)
