@@ -4,8 +4,9 @@ seeded inputs.
 
 The page's split kernel and Block are written for any stream count; the library
 runs four streams on its single-pass kernels and other counts on one kernel per
-step. Sizes leave partial 16-token tiles and partial 64-column tiles of the
-flattened hc*d axis. Tolerances and the comparison rule are in tests/parity.py.
+step. Sizes leave partial 64-token tiles and partial 64-column tiles of the
+flattened hc*d axis, and reach the smallest width d = 8. Tolerances and the
+comparison rule are in tests/parity.py.
 """
 import pytest
 import torch
@@ -17,7 +18,7 @@ from parity import TOL_BF16, TOL_F32, check, rho_for
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
-HCS = [1, 2, 3, 5, 8]
+HCS = [1, 2, 3, 5, 6, 7, 8]   # the projection's column-tile counts R = ceil((2+hc)hc / 16): 1, 3, 4, 5
 
 
 def to_dev(t):
@@ -78,7 +79,8 @@ def test_pre_and_post(hc_, dtype, n, d):
 # ------------------------------------------------------------------- mixes
 @pytest.mark.parametrize("hc_", HCS)
 @pytest.mark.parametrize("dtype,n,d", [(torch.float32, 16, 256), (torch.float32, 37, 264),
-                                       (torch.bfloat16, 37, 264), (torch.bfloat16, 70, 5120)])
+                                       (torch.bfloat16, 37, 264), (torch.bfloat16, 70, 5120),
+                                       (torch.bfloat16, 3, 8), (torch.float32, 130, 8)])
 def test_mixes(hc_, dtype, n, d):
     g = hc_inputs.generator(50 + hc_)
     fn, _, _ = hc_inputs.mix_params(g, hc_, d, "ones")
@@ -105,9 +107,10 @@ def _block_inputs(hc_, dtype, n, d, seed):
     return x, attn, ffn, f_attn, f_ffn, prev
 
 
-@pytest.mark.parametrize("hc_,iters", [(1, 20), (2, 20), (3, 5), (4, 5), (5, 20), (8, 20), (8, 1)])
+@pytest.mark.parametrize("hc_,iters", [(1, 20), (2, 20), (3, 5), (4, 5), (5, 20), (6, 20), (7, 3), (8, 20),
+                                       (8, 1)])
 @pytest.mark.parametrize("dtype,n,d", [(torch.float32, 16, 256), (torch.bfloat16, 37, 264),
-                                       (torch.bfloat16, 64, 5120)])
+                                       (torch.bfloat16, 64, 5120), (torch.bfloat16, 5, 8)])
 def test_block(hc_, iters, dtype, n, d):
     """Attention boundary, FFN boundary (expand + coefficients + collapse with the
     attention's pre), FFN expand. The FFN coefficients come from the rounded streams
