@@ -193,3 +193,50 @@ def test_huge_shapes_rejected(fn):
         assert _mixes(n=1 << 40, d=1 << 20) == SHAPE
     else:
         assert _fused(n=1 << 40, d=1 << 20) == SHAPE
+
+
+def test_generic_stream_count_spans():
+    """Stream counts other than four size every span by hc: outputs that overlap at
+    hc = 8 but would not at hc = 4 are rejected, and neighbouring buffers placed
+    exactly hc-sized apart are accepted by validation (which then reaches the
+    launch; only the error cases are run here)."""
+    n = 16
+    # split, hc = 8: pre is n*8*4 = 512 B; post placed 256 B after pre overlaps it
+    assert _split(hc_=8, pre=0x40000000, post=0x40000000 + 256, comb=0x40010000,
+                  mixes=0x50000000) == ALIAS
+    # comb (n*64*4 = 4096 B at hc = 8) overlapping mixes' tail
+    M8 = (2 + 8) * 8
+    assert _split(hc_=8, mixes=0x50000000, pre=0x40000000, post=0x40001000,
+                  comb=0x50000000 + n * M8 * 4 - 16) == ALIAS
+    # pre, hc = 2: x is n*2*d elements; y right after x's 2 streams but inside 4 streams
+    d = 256
+    assert _pre(hc_=2, x=A, y=A + n * 2 * d * 2 - 16, d=d) == ALIAS
+    # post, hc = 8: out partially overlapping the 8-stream residual
+    assert hc.lib().hc_post(P(A), P(B), 1, P(C), P(C + 4096), n, 8, d, P(B + n * 8 * d * 2 - 32),
+                            None) == ALIAS
+    # mixes, hc = 3: the workspace must cover the unfused plan
+    ws3 = hc.workspace_size(n, 3, d)
+    assert hc.lib().hc_mixes(P(A), 1, n, 3, d, P(B), 1e-20, P(C), P(0x60000000), ws3 - 1, None) == WS
+
+
+def test_fused_generic_validation():
+    """hc_fused_step with hc = 5: null, workspace and alias rules use the unfused plan
+    and hc-sized spans."""
+    def fused(**kw):
+        base = dict(res=A, pre_mix=0x50000000, fn=B, scale=C, base=C + 4096, n=16, d=256, dtype=1, iters=20,
+                    y=0x60000000, pre=0x70000000, post=0x70001000, comb=0x70002000, mixes=None, ws=0x40000000,
+                    ws_bytes=1 << 22, f_prev=None, post_prev=None, comb_prev=None, so=None)
+        base.update(kw)
+        return hc.lib().hc_fused_step(P(base["res"]), P(base["f_prev"]), P(base["post_prev"]),
+                                      P(base["comb_prev"]), P(base["pre_mix"]), P(base["fn"]), P(base["scale"]),
+                                      P(base["base"]), base["n"], 5, base["d"], base["dtype"], 1e-20,
+                                      base["iters"], 1e-6, P(base["so"]), P(base["y"]), P(base["pre"]),
+                                      P(base["post"]), P(base["comb"]), P(base["mixes"]), P(base["ws"]),
+                                      base["ws_bytes"], None)
+    assert fused(n=0) == OK
+    assert fused(ws_bytes=hc.workspace_size(16, 5, 256) - 1) == WS
+    assert fused(pre=None) == NULL
+    assert fused(post=0x70000000 + 16 * 5 * 4 - 16) == ALIAS    # post overlaps pre's last 16 bytes
+    assert fused(comb=0x70001000 + 16 * 5 * 4 - 16) == ALIAS    # comb overlaps post
+    assert fused(f_prev=0x58000000, post_prev=0x59000000, comb_prev=0x59001000,
+                 so=A + 16) == ALIAS                           # partial overlap with residual
