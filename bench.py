@@ -261,6 +261,33 @@ def long_prefill_steady(dev, steps: int = 8):
     return res
 
 
+def split_stress(dev, steps: int = 20):
+    """The split stage alone (hc_split_sinkhorn) on the stress set: 1,048,576 rows of 24
+    logits (~N(0, 3), 5% with one comb logit +40), 20 rounds. 96 B in and 96 B out
+    per row."""
+    import torch
+    import hc_inputs
+    import hyper_connection_residual_mixes_amd as hc
+    st = hc_inputs.stress(seed=0, device=dev)
+    m, s, b = st["mixes"], st["scale"], st["base"]
+    n = m.shape[0]
+    out = (torch.empty(n, 4, device=dev), torch.empty(n, 4, device=dev), torch.empty(n, 4, 4, device=dev))
+    for _ in range(3):
+        hc.hc_split_sinkhorn(m, s, b, out=out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        hc.hc_split_sinkhorn(m, s, b, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / steps
+    ab = n * (96 + 96) + 96 + 12
+    return {"workload": f"split + Sinkhorn only, {n} rows x 24 logits, 20 rounds",
+            "us": sec * 1e6, "rows_per_s": n / sec, "algorithmic_bytes": ab,
+            "achieved_gb_s": ab / sec / 1e9, "frac": ab / sec / 1e9 / PEAK_HBM_GBS}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -401,6 +428,7 @@ def main():
     next_rows["decode"] = decode_latency(dev)
     next_rows["generic_hc"] = generic_hc_blocks(dev)
     next_rows["long_prefill"] = long_prefill_steady(dev)
+    next_rows["split_stress"] = split_stress(dev)
     result["next_rows"] = next_rows
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on every input set", file=sys.stderr, flush=True)
