@@ -71,11 +71,18 @@ def _check(fn: str, status: int):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # an int: ctypes converts it for the c_void_p argument
+    return None if t is None else t.data_ptr()
+
+
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream(device):
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    """The current HIP stream of `device` (torch's), as an address."""
+    if _raw_stream is not None and device.index is not None:
+        return _raw_stream(device.index)
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -111,9 +118,9 @@ def workspace_size(n: int, hc: int, d: int) -> int:
 
 
 def _workspace(n, hc, d, device, workspace):
-    need = workspace_size(n, hc, d)
+    """The caller's workspace (its size is checked by the library), or a new one."""
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+        workspace = torch.empty(max(workspace_size(n, hc, d), 16), dtype=torch.uint8, device=device)
     return workspace, workspace.numel() * workspace.element_size()
 
 
