@@ -18,7 +18,10 @@
 //   mixes_partial_kernel    64 tokens x one slice of the flattened hc*d axis per
 //                           workgroup: the (2+hc)*hc partial dot products (fp32
 //                           MFMA) and the partial sum of squares, from LDS tiles
-//                           of 64 columns.
+//                           of 64 columns (fp32 streams).
+//   mixes_partial_bf16_kernel  the same partial rows for bf16 streams: 128 tokens
+//                           per workgroup, bf16 MFMAs on the exact stream values
+//                           and on the weights split into three bf16 terms.
 //   mixes_finalize_kernel   a wave per token: partial rows summed over the slices
 //                           in order, scaled by the RMS statistic.
 //
@@ -193,10 +196,10 @@ __global__ __launch_bounds__(kGBlock) void post_generic_kernel(const void* __res
 }
 
 // ------------------------------------------------------------- projection
-// Workgroup (tile, slice): tokens tile*64 .. +64 and flattened columns
-// [slice * cols_per_split, +cols_per_split), walked in tiles of 64 columns
-// staged in LDS (streams converted to fp32, and the hc_fn rows; rows of the hc_fn
-// tile past the last mix are zero). The next tile is fetched into registers
+// fp32 streams. Workgroup (tile, slice): tokens tile*64 .. +64 and flattened
+// columns [slice * cols_per_split, +cols_per_split), walked in tiles of 64
+// columns staged in LDS (the streams and the hc_fn rows; rows of the hc_fn tile
+// past the last mix are zero). The next tile is fetched into registers
 // while the current one is multiplied. Wave w multiplies its 16 tokens by the R
 // 16-wide column tiles of hc_fn with v_mfma_f32_16x16x4f32 (exact fp32 products,
 // fp32 accumulation): lane l (row l % 16, group g = l / 16) feeds, at each of the
@@ -211,31 +214,26 @@ typedef float floatx4_g __attribute__((ext_vector_type(4)));
 
 // One 64-column tile as fetched from memory, held in registers until it is
 // written to LDS: lane tid owns stream columns (tid % 4) * 16 .. +16 of token
-// tid / 4 (raw words), and float4 slots tid + 256 r of the hc_fn tile (16 slots
-// per row, rows past the last mix read as zero).
-template <bool kBf16, int R>
+// tid / 4, and float4 slots tid + 256 r of the hc_fn tile (16 slots per row, rows
+// past the last mix read as zero).
+template <int R>
 struct GenericStage {
-    uint4 xw[kBf16 ? 2 : 4];
+    float4 xv[4];
     float4 wv[R];
 };
 
-template <bool kBf16, int R>
-__device__ __forceinline__ void stage_load(GenericStage<kBf16, R>& st, const void* x, const float* hc_fn, int64_t n,
-                                           int M, int64_t K, int64_t t0, int64_t c0, int64_t c_end) {
+template <int R>
+__device__ __forceinline__ void stage_load(GenericStage<R>& st, const float* x, const float* hc_fn, int64_t n, int M,
+                                           int64_t K, int64_t t0, int64_t c0, int64_t c_end) {
     const int tid = threadIdx.x, row = tid >> 2, col = (tid & 3) * 16;
     const int64_t t = t0 + row;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {   // two halves of 8 columns; K and the slice bounds are multiples of 8
         const int64_t c = c0 + col + 8 * h;
         const bool ok = t < n && c < c_end;
-        if constexpr (kBf16) {
-            st.xw[h] = ok ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + t * K + c)
-                          : make_uint4(0, 0, 0, 0);
-        } else {
-            const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(x) + t * K + c);
-            st.xw[2 * h] = ok ? p[0] : make_uint4(0, 0, 0, 0);
-            st.xw[2 * h + 1] = ok ? p[1] : make_uint4(0, 0, 0, 0);
-        }
+        const float4* p = reinterpret_cast<const float4*>(x + t * K + c);
+        st.xv[2 * h] = ok ? p[0] : make_float4(0.f, 0.f, 0.f, 0.f);
+        st.xv[2 * h + 1] = ok ? p[1] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -246,25 +244,12 @@ __device__ __forceinline__ void stage_load(GenericStage<kBf16, R>& st, const voi
     }
 }
 
-template <bool kBf16, int R>
-__device__ __forceinline__ void stage_store(const GenericStage<kBf16, R>& st, float* xs, float* ws) {
+template <int R>
+__device__ __forceinline__ void stage_store(const GenericStage<R>& st, float* xs, float* ws) {
     const int tid = threadIdx.x, row = tid >> 2, col = (tid & 3) * 16;
     float4* dst = reinterpret_cast<float4*>(xs + row * kGRow + col);
-    if constexpr (kBf16) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint32_t u[4] = {st.xw[h].x, st.xw[h].y, st.xw[h].z, st.xw[h].w};
-            dst[2 * h] = make_float4(__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u),
-                                     __uint_as_float(u[1] << 16), __uint_as_float(u[1] & 0xffff0000u));
-            dst[2 * h + 1] = make_float4(__uint_as_float(u[2] << 16), __uint_as_float(u[2] & 0xffff0000u),
-                                         __uint_as_float(u[3] << 16), __uint_as_float(u[3] & 0xffff0000u));
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            dst[i] = make_float4(__uint_as_float(st.xw[i].x), __uint_as_float(st.xw[i].y),
-                                 __uint_as_float(st.xw[i].z), __uint_as_float(st.xw[i].w));
-    }
+    for (int i = 0; i < 4; ++i) dst[i] = st.xv[i];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int q = tid + kGBlock * r, i = q / (kGCols / 4), lc = (q % (kGCols / 4)) * 4;
@@ -272,8 +257,8 @@ __device__ __forceinline__ void stage_store(const GenericStage<kBf16, R>& st, fl
     }
 }
 
-template <bool kBf16, int R>
-__global__ __launch_bounds__(kGBlock) void mixes_partial_kernel(const void* __restrict__ x,
+template <int R>
+__global__ __launch_bounds__(kGBlock) void mixes_partial_kernel(const float* __restrict__ x,
                                                                 const float* __restrict__ hc_fn, int64_t n,
                                                                 int hc, int64_t d, int cols_per_split,
                                                                 int nsplit, float* __restrict__ part, int pg) {
@@ -292,14 +277,14 @@ __global__ __launch_bounds__(kGBlock) void mixes_partial_kernel(const void* __re
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = floatx4_g{0.f, 0.f, 0.f, 0.f};
     float ss = 0.f;
-    GenericStage<kBf16, R> st;
-    stage_load<kBf16, R>(st, x, hc_fn, n, M, K, t0, c_begin, c_end);
+    GenericStage<R> st;
+    stage_load<R>(st, x, hc_fn, n, M, K, t0, c_begin, c_end);
     for (int64_t c0 = c_begin; c0 < c_end; c0 += kGCols) {
         __syncthreads();   // the previous tile is consumed
-        stage_store<kBf16, R>(st, xs, ws);
+        stage_store<R>(st, xs, ws);
         __syncthreads();
         if (c0 + kGCols < c_end)   // the next tile's loads run under this tile's MFMAs
-            stage_load<kBf16, R>(st, x, hc_fn, n, M, K, t0, c0 + kGCols, c_end);
+            stage_load<R>(st, x, hc_fn, n, M, K, t0, c0 + kGCols, c_end);
         const float* xa = xs + (w * 16 + r16) * kGRow + 16 * g;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
@@ -336,6 +321,207 @@ __global__ __launch_bounds__(kGBlock) void mixes_partial_kernel(const void* __re
     if (g == 0 && ts < n) part[((int64_t)slice * n + ts) * pg + M] = ss;
 }
 
+// bf16 streams. The products of bf16 stream values with bf16 numbers are exact
+// in fp32, so the projection runs on bf16 MFMAs once each fp32 weight is split
+// into three bf16 terms (w ~ hi + mid + lo, about 24 significant bits), each
+// multiplied and accumulated in fp32 (hi, then mid, then lo). Workgroup (tile,
+// slice): 4 waves x kBT 16-token row tiles, so that every B operand read from LDS
+// feeds kBT MFMAs and every weight fetched from L2 serves 64 kBT tokens: four row
+// tiles when there are three or more column tiles of mixes (hc >= 5), two below,
+// where the weights are few and shorter tiles give more workgroups. The hc_fn tile is split once, when it is written to LDS, into three
+// bf16 planes; the stream tile stays bf16. LDS rows hold 64 columns padded to
+// 144 bytes, so that 16 consecutive rows read at one column cover distinct
+// banks. Per 64-column tile and 32-column k-block, lane l (row r16 = l % 16,
+// k-group g = l / 16) reads 8 columns 8 g .. 8 g + 7 of its row tiles' tokens
+// (A) and of mix row r*16 + r16 in each plane (B), as the 16x16x32 bf16 MFMA
+// lays out its operands. The sum of squares is the diagonal of A times A (exact
+// products, fp32 accumulation).
+typedef __bf16 bf16x8_g __attribute__((ext_vector_type(8)));
+__host__ __device__ constexpr int bf16_row_tiles(int R) { return R <= 2 ? 2 : 4; }   // per wave
+constexpr int kBRow = kGCols + 8;        // LDS row stride of the bf16 tiles (elements)
+__host__ __device__ constexpr int bf16_x_slots(int R) { return 64 * bf16_row_tiles(R) * kGCols / 8 / kGBlock; }
+
+__device__ __forceinline__ float bf16_lo_g(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi_g(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 weights as three packed bf16 pairs: hi = bf16(w), mid = bf16(w - hi),
+// lo = bf16(w - hi - mid); both differences are exact in fp32.
+__device__ __forceinline__ void split3_pair(float a, float b, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+    hi = pack2(a, b);
+    const float ra = a - bf16_lo_g(hi), rb = b - bf16_hi_g(hi);
+    mid = pack2(ra, rb);
+    lo = pack2(ra - bf16_lo_g(mid), rb - bf16_hi_g(mid));
+}
+
+// Raw buffer loads: a wave-uniform resource (base, byte range) plus a per-lane
+// offset and a wave-uniform scalar offset. The range check covers the per-lane
+// offset only, so a lane whose load must return zero gets kOffMaskedG.
+typedef unsigned int u32x4_g __attribute__((ext_vector_type(4)));
+constexpr uint32_t kOffMaskedG = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_g(const void* base, int64_t bytes) {
+    const int64_t b = bytes < 0 ? 0 : (bytes > 0x7ffffff0 ? 0x7ffffff0 : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)b, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x4_g v =
+        __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, __builtin_amdgcn_readfirstlane((int)soff), 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// One 64-column tile in registers: stream slot p of thread tid is token row
+// tid / 8 + 32 p, columns (tid % 8) * 8 .. +8 (8 lanes cover a row's 128 bytes);
+// hc_fn slot r is row tid / 16 + 16 r, columns (tid % 16) * 4 .. +4. Each slot
+// has a resource starting at its first row and ending at the last token or mix
+// row, so that rows past either read as zero; one lane offset (the row within
+// the slot and the column) serves every slot, the tile's column is the scalar
+// offset.
+template <int R>
+struct Bf16Stage {
+    uint4 xw[bf16_x_slots(R)];
+    uint4 wv[R];
+};
+
+template <int R>
+struct Bf16Src {
+    __amdgpu_buffer_rsrc_t x[bf16_x_slots(R)];
+    __amdgpu_buffer_rsrc_t w[R];
+    uint32_t xoff, woff;   // lane offsets (bytes)
+};
+
+template <int R>
+__device__ __forceinline__ void make_src_bf16(Bf16Src<R>& src, const uint16_t* x, const float* hc_fn, int64_t n,
+                                              int M, int64_t K, int64_t t0) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int p = 0; p < bf16_x_slots(R); ++p) {
+        const int64_t row0 = t0 + 32 * p;
+        src.x[p] = rsrc_g(x + row0 * K, (n - row0) * K * 2);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) src.w[r] = rsrc_g(hc_fn + (int64_t)16 * r * K, (int64_t)(M - 16 * r) * K * 4);
+    src.xoff = (uint32_t)((int64_t)(tid >> 3) * K * 2 + (tid & 7) * 16);
+    src.woff = (uint32_t)((int64_t)(tid >> 4) * K * 4 + (tid & 15) * 16);
+}
+
+template <int R>
+__device__ __forceinline__ void stage_load_bf16(Bf16Stage<R>& st, const Bf16Src<R>& src, int64_t c0, int64_t c_end) {
+    const int tid = threadIdx.x;
+    const uint32_t xo = c0 + (tid & 7) * 8 < c_end ? src.xoff : kOffMaskedG;     // K, slice bounds: multiples of 8
+    const uint32_t wo = c0 + (tid & 15) * 4 < c_end ? src.woff : kOffMaskedG;
+#pragma unroll
+    for (int p = 0; p < bf16_x_slots(R); ++p) st.xw[p] = bload16(src.x[p], xo, (uint32_t)(c0 * 2));
+#pragma unroll
+    for (int r = 0; r < R; ++r) st.wv[r] = bload16(src.w[r], wo, (uint32_t)(c0 * 4));
+}
+
+// ws: three planes (hi, mid, lo) of 16 R rows each.
+template <int R>
+__device__ __forceinline__ void stage_store_bf16(const Bf16Stage<R>& st, uint16_t* xs, uint16_t* ws) {
+    const int tid = threadIdx.x, col = (tid & 7) * 8;
+#pragma unroll
+    for (int p = 0; p < bf16_x_slots(R); ++p)
+        *reinterpret_cast<uint4*>(xs + ((tid >> 3) + 32 * p) * kBRow + col) = st.xw[p];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int i = (tid >> 4) + 16 * r, lc = (tid & 15) * 4;
+        uint32_t h0, m0, l0, h1, m1, l1;
+        split3_pair(__uint_as_float(st.wv[r].x), __uint_as_float(st.wv[r].y), h0, m0, l0);
+        split3_pair(__uint_as_float(st.wv[r].z), __uint_as_float(st.wv[r].w), h1, m1, l1);
+        uint16_t* row = ws + i * kBRow + lc;
+        *reinterpret_cast<uint2*>(row) = make_uint2(h0, h1);
+        *reinterpret_cast<uint2*>(row + 16 * R * kBRow) = make_uint2(m0, m1);
+        *reinterpret_cast<uint2*>(row + 32 * R * kBRow) = make_uint2(l0, l1);
+    }
+}
+
+template <int R>
+__global__ __launch_bounds__(kGBlock, 2) void mixes_partial_bf16_kernel(const uint16_t* __restrict__ x,
+                                                                        const float* __restrict__ hc_fn, int64_t n,
+                                                                        int hc, int64_t d, int cols_per_split,
+                                                                        int nsplit, float* __restrict__ part,
+                                                                        int pg) {
+    constexpr int kBT = bf16_row_tiles(R), kBTok = 64 * kBT;
+    __shared__ __attribute__((aligned(16))) uint16_t xs[kBTok * kBRow];
+    __shared__ __attribute__((aligned(16))) uint16_t ws[3 * 16 * R * kBRow];
+    const int M = (2 + hc) * hc;
+    const int64_t K = (int64_t)hc * d;
+    const int64_t tile = blockIdx.x / nsplit;
+    const int slice = (int)(blockIdx.x - tile * nsplit);
+    const int64_t t0 = tile * kBTok;
+    const int64_t c_begin = (int64_t)slice * cols_per_split;
+    const int64_t c_end = c_begin + cols_per_split < K ? c_begin + cols_per_split : K;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int r16 = lane & 15, g = lane >> 4;
+    floatx4_g acc[kBT][R], gram[kBT];
+#pragma unroll
+    for (int T = 0; T < kBT; ++T) {
+        gram[T] = floatx4_g{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[T][r] = floatx4_g{0.f, 0.f, 0.f, 0.f};
+    }
+    Bf16Src<R> src;
+    make_src_bf16<R>(src, x, hc_fn, n, M, K, t0);
+    Bf16Stage<R> st;
+    stage_load_bf16<R>(st, src, c_begin, c_end);
+    const uint16_t* xa = xs + (w * 16 * kBT + r16) * kBRow + g * 8;
+    const uint16_t* wb = ws + r16 * kBRow + g * 8;
+    for (int64_t c0 = c_begin; c0 < c_end; c0 += kGCols) {
+        __syncthreads();   // the previous tile is consumed
+        stage_store_bf16<R>(st, xs, ws);
+        __syncthreads();
+        if (c0 + kGCols < c_end)   // the next tile's loads run under this tile's MFMAs
+            stage_load_bf16<R>(st, src, c0 + kGCols, c_end);
+#pragma unroll
+        for (int kb = 0; kb < kGCols / 32; ++kb) {
+            bf16x8_g a[kBT], b[2][3];
+#pragma unroll
+            for (int T = 0; T < kBT; ++T)
+                a[T] = *reinterpret_cast<const bf16x8_g*>(xa + T * 16 * kBRow + kb * 32);
+#pragma unroll
+            for (int plane = 0; plane < 3; ++plane)
+                b[0][plane] = *reinterpret_cast<const bf16x8_g*>(wb + plane * 16 * R * kBRow + kb * 32);
+            // column tile r + 1's operands are read while tile r is multiplied
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                if (r + 1 < R) {
+#pragma unroll
+                    for (int plane = 0; plane < 3; ++plane)
+                        b[(r + 1) & 1][plane] = *reinterpret_cast<const bf16x8_g*>(
+                            wb + ((r + 1) * 16 + plane * 16 * R) * kBRow + kb * 32);
+                }
+#pragma unroll
+                for (int plane = 0; plane < 3; ++plane)
+#pragma unroll
+                    for (int T = 0; T < kBT; ++T)
+                        acc[T][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[T], b[r & 1][plane], acc[T][r], 0, 0,
+                                                                            0);
+            }
+#pragma unroll
+            for (int T = 0; T < kBT; ++T)
+                gram[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[T], a[T], gram[T], 0, 0, 0);
+        }
+    }
+    // accumulator lane l of row tile T: tokens T*16 + 4 g + i (i < 4) of the wave's, mix r*16 + r16
+#pragma unroll
+    for (int T = 0; T < kBT; ++T) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int mix = r * 16 + r16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t t = t0 + w * 16 * kBT + T * 16 + 4 * g + i;
+                if (t < n && mix < M) part[((int64_t)slice * n + t) * pg + mix] = acc[T][r][i];
+            }
+        }
+        // the diagonal: lane r16 == 4 g + i holds token T*16 + r16's sum of squares
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t t = t0 + w * 16 * kBT + T * 16 + r16;
+            if (r16 == 4 * g + i && t < n) part[((int64_t)slice * n + t) * pg + M] = gram[T][i];
+        }
+    }
+}
+
 // A wave per token: lane l sums entries l and l + 64 of the partial rows over the
 // slices in order, then scales the dots by 1 / sqrt(sum of squares / (hc d) + eps).
 __global__ __launch_bounds__(kGBlock) void mixes_finalize_kernel(const float* __restrict__ part, int nsplit,
@@ -347,11 +533,22 @@ __global__ __launch_bounds__(kGBlock) void mixes_finalize_kernel(const float* __
     const int M = (2 + hc) * hc;
     const int i0 = lane, i1 = lane + 64;
     float a0 = 0.f, a1 = 0.f;
-#pragma unroll 8
-    for (int s = 0; s < nsplit; ++s) {
-        const float* row = part + ((int64_t)s * n + t) * pg;
-        if (i0 <= M) a0 += row[i0];
-        if (i1 <= M) a1 += row[i1];
+    // 16 slices' loads are issued before they are added (in slice order; a
+    // missing slice adds +0)
+    for (int s0 = 0; s0 < nsplit; s0 += 16) {
+        float v0[16], v1[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float* row = part + ((int64_t)(s0 + i) * n + t) * pg;
+            const bool ok = s0 + i < nsplit;
+            v0[i] = ok && i0 <= M ? row[i0] : 0.f;
+            v1[i] = ok && i1 <= M ? row[i1] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            a0 += v0[i];
+            a1 += v1[i];
+        }
     }
     const float ss = M < 64 ? __shfl(a0, M) : __shfl(a1, M - 64);
     const float rstd = 1.0f / sqrtf(ss / (float)((int64_t)hc * d) + norm_eps);
@@ -371,47 +568,87 @@ struct GenericPlan {
     size_t total_bytes;
 };
 
-GenericPlan plan_generic(int64_t n, int hc, int64_t d) {
-    GenericPlan p{};
-    const int M = (2 + hc) * hc;
-    const int64_t K = (int64_t)hc * d;
-    p.tiles = ceil_div_g(n, kGTok);
+struct SplitShape {
+    int64_t tiles;
+    int cols_per_split;
+    int nsplit;
+};
+
+// Token tiles of `tok` tokens x slices of whole 64-column tiles, about two
+// workgroups per CU.
+SplitShape split_shape(int64_t n, int64_t K, int tok) {
+    SplitShape s{};
+    s.tiles = ceil_div_g(n, tok);
     const int64_t ncols = ceil_div_g(K, kGCols);
-    int64_t ns = ceil_div_g(512, p.tiles > 0 ? p.tiles : 1);   // about two workgroups per CU
+    int64_t ns = ceil_div_g(512, s.tiles > 0 ? s.tiles : 1);
     if (ns > ncols) ns = ncols;
     if (ns > kGMaxSplit) ns = kGMaxSplit;
     if (ns < 1) ns = 1;
-    p.cols_per_split = (int)(ceil_div_g(ncols, ns) * kGCols);
-    p.nsplit = (int)ceil_div_g(K, p.cols_per_split);
+    s.cols_per_split = (int)(ceil_div_g(ncols, ns) * kGCols);
+    s.nsplit = (int)ceil_div_g(K, s.cols_per_split);
+    return s;
+}
+
+// The workspace layout does not depend on the stream dtype: the partial rows of
+// the larger of the two plans, then the scratch mixes.
+GenericPlan plan_generic(int64_t n, int hc, int64_t d, bool bf16) {
+    GenericPlan p{};
+    const int M = (2 + hc) * hc;
+    const int64_t K = (int64_t)hc * d;
+    const SplitShape f = split_shape(n, K, kGTok), b = split_shape(n, K, 64 * bf16_row_tiles((M + 15) / 16));
+    const SplitShape& s = bf16 ? b : f;
+    p.tiles = s.tiles;
+    p.cols_per_split = s.cols_per_split;
+    p.nsplit = s.nsplit;
     p.pg = (M + 1 + 3) & ~3;
     p.part_bytes = (size_t)p.nsplit * (size_t)n * (size_t)p.pg * sizeof(float);
-    p.mixes_offset = (p.part_bytes + 255) & ~size_t(255);
+    const int ns_max = f.nsplit > b.nsplit ? f.nsplit : b.nsplit;
+    p.mixes_offset = ((size_t)ns_max * (size_t)n * (size_t)p.pg * sizeof(float) + 255) & ~size_t(255);
     p.total_bytes = p.mixes_offset + (size_t)n * (size_t)M * sizeof(float);
     return p;
 }
 
-template <bool kBf16>
-void launch_partial(const GenericPlan& p, const void* x, const float* hc_fn, int64_t n, int hc, int64_t d,
-                    float* part, hipStream_t stream) {
+void launch_partial_f32(const GenericPlan& p, const void* xv, const float* hc_fn, int64_t n, int hc, int64_t d,
+                        float* part, hipStream_t stream) {
     const int M = (2 + hc) * hc;
+    const float* x = static_cast<const float*>(xv);
     const dim3 grid((unsigned)(p.tiles * p.nsplit)), block(kGBlock);
     switch ((M + 15) / 16) {
-        case 1: hipLaunchKernelGGL((mixes_partial_kernel<kBf16, 1>), grid, block, 0, stream, x, hc_fn, n, hc, d,
+        case 1: hipLaunchKernelGGL((mixes_partial_kernel<1>), grid, block, 0, stream, x, hc_fn, n, hc, d,
                                    p.cols_per_split, p.nsplit, part, p.pg); break;
-        case 2: hipLaunchKernelGGL((mixes_partial_kernel<kBf16, 2>), grid, block, 0, stream, x, hc_fn, n, hc, d,
+        case 2: hipLaunchKernelGGL((mixes_partial_kernel<2>), grid, block, 0, stream, x, hc_fn, n, hc, d,
                                    p.cols_per_split, p.nsplit, part, p.pg); break;
-        case 3: hipLaunchKernelGGL((mixes_partial_kernel<kBf16, 3>), grid, block, 0, stream, x, hc_fn, n, hc, d,
+        case 3: hipLaunchKernelGGL((mixes_partial_kernel<3>), grid, block, 0, stream, x, hc_fn, n, hc, d,
                                    p.cols_per_split, p.nsplit, part, p.pg); break;
-        case 4: hipLaunchKernelGGL((mixes_partial_kernel<kBf16, 4>), grid, block, 0, stream, x, hc_fn, n, hc, d,
+        case 4: hipLaunchKernelGGL((mixes_partial_kernel<4>), grid, block, 0, stream, x, hc_fn, n, hc, d,
                                    p.cols_per_split, p.nsplit, part, p.pg); break;
-        default: hipLaunchKernelGGL((mixes_partial_kernel<kBf16, 5>), grid, block, 0, stream, x, hc_fn, n, hc, d,
+        default: hipLaunchKernelGGL((mixes_partial_kernel<5>), grid, block, 0, stream, x, hc_fn, n, hc, d,
+                                    p.cols_per_split, p.nsplit, part, p.pg); break;
+    }
+}
+
+void launch_partial_bf16(const GenericPlan& p, const void* x, const float* hc_fn, int64_t n, int hc, int64_t d,
+                         float* part, hipStream_t stream) {
+    const int M = (2 + hc) * hc;
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    const dim3 grid((unsigned)(p.tiles * p.nsplit)), block(kGBlock);
+    switch ((M + 15) / 16) {
+        case 1: hipLaunchKernelGGL((mixes_partial_bf16_kernel<1>), grid, block, 0, stream, xb, hc_fn, n, hc, d,
+                                   p.cols_per_split, p.nsplit, part, p.pg); break;
+        case 2: hipLaunchKernelGGL((mixes_partial_bf16_kernel<2>), grid, block, 0, stream, xb, hc_fn, n, hc, d,
+                                   p.cols_per_split, p.nsplit, part, p.pg); break;
+        case 3: hipLaunchKernelGGL((mixes_partial_bf16_kernel<3>), grid, block, 0, stream, xb, hc_fn, n, hc, d,
+                                   p.cols_per_split, p.nsplit, part, p.pg); break;
+        case 4: hipLaunchKernelGGL((mixes_partial_bf16_kernel<4>), grid, block, 0, stream, xb, hc_fn, n, hc, d,
+                                   p.cols_per_split, p.nsplit, part, p.pg); break;
+        default: hipLaunchKernelGGL((mixes_partial_bf16_kernel<5>), grid, block, 0, stream, xb, hc_fn, n, hc, d,
                                     p.cols_per_split, p.nsplit, part, p.pg); break;
     }
 }
 
 }  // namespace
 
-size_t generic_workspace_bytes(int64_t n, int hc, int64_t d) { return plan_generic(n, hc, d).total_bytes; }
+size_t generic_workspace_bytes(int64_t n, int hc, int64_t d) { return plan_generic(n, hc, d, true).total_bytes; }
 
 hipError_t launch_split_generic(const float* mixes, const float* scale, const float* base, int64_t n, int hc,
                                 int iters, float eps, float* pre, float* post, float* comb, hipStream_t stream) {
@@ -444,12 +681,12 @@ hipError_t launch_post_generic(const void* f, const void* res, bool bf16, const 
 
 hipError_t launch_mixes_generic(const void* x, bool bf16, int64_t n, int hc, int64_t d, const float* hc_fn,
                                 float norm_eps, float* mixes, void* workspace, hipStream_t stream) {
-    const GenericPlan p = plan_generic(n, hc, d);
+    const GenericPlan p = plan_generic(n, hc, d, bf16);
     float* part = static_cast<float*>(workspace);
     if (bf16)
-        launch_partial<true>(p, x, hc_fn, n, hc, d, part, stream);
+        launch_partial_bf16(p, x, hc_fn, n, hc, d, part, stream);
     else
-        launch_partial<false>(p, x, hc_fn, n, hc, d, part, stream);
+        launch_partial_f32(p, x, hc_fn, n, hc, d, part, stream);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     hipLaunchKernelGGL(mixes_finalize_kernel, dim3((unsigned)ceil_div_g(n, kGBlock / 64)), dim3(kGBlock), 0, stream,
                        part, p.nsplit, p.pg, n, hc, d, norm_eps, mixes);
@@ -457,7 +694,7 @@ hipError_t launch_mixes_generic(const void* x, bool bf16, int64_t n, int hc, int
 }
 
 hipError_t launch_fused_generic(const GenericRequest& r, hipStream_t stream) {
-    const GenericPlan p = plan_generic(r.n, r.hc, r.d);
+    const GenericPlan p = plan_generic(r.n, r.hc, r.d, r.bf16);
     const void* src = r.res;
     if (r.f_prev) {
         if (hipError_t e = launch_post_generic(r.f_prev, r.res, r.bf16, r.post_prev, r.comb_prev, r.n, r.hc, r.d,

@@ -80,7 +80,8 @@ def test_pre_and_post(hc_, dtype, n, d):
 @pytest.mark.parametrize("hc_", HCS)
 @pytest.mark.parametrize("dtype,n,d", [(torch.float32, 16, 256), (torch.float32, 37, 264),
                                        (torch.bfloat16, 37, 264), (torch.bfloat16, 70, 5120),
-                                       (torch.bfloat16, 3, 8), (torch.float32, 130, 8)])
+                                       (torch.bfloat16, 3, 8), (torch.float32, 130, 8),
+                                       (torch.bfloat16, 300, 264)])
 def test_mixes(hc_, dtype, n, d):
     g = hc_inputs.generator(50 + hc_)
     fn, _, _ = hc_inputs.mix_params(g, hc_, d, "ones")
