@@ -152,3 +152,26 @@ def test_fused_exact_inputs_and_in_place(hc_):
     sync()
     check(f"hc={hc_} streams (in place)", xd, ref2["streams"], TOL_BF16)
     check(f"hc={hc_} y after expand", got2["y"], ref2["y"], TOL_BF16)
+
+
+@pytest.mark.parametrize("hc_", [2, 8])
+def test_block_full_size_sampled(hc_):
+    """The prefill block at two and eight streams (4096 tokens x 5120 bf16, 1% x50
+    outliers: the inputs and launch configuration the benchmark times). Every step is
+    per token, so the oracle runs on 48 sampled tokens only; those tokens of every
+    output are compared, with the tolerances of test_block."""
+    w = hc_inputs.Workload(f"prefill_hc{hc_}", 1, 4096, 5120, torch.bfloat16, hc=hc_)
+    inp = hc_inputs.block_inputs(w, seed=0, outlier_frac=0.01)
+    pi = oracle.hc_split_sinkhorn(*inp["prev"], hc_mult=hc_)[0]
+    got = hc.block(*to_dev((inp["x"], pi)), to_dev(inp["attn"]), to_dev(inp["ffn"]),
+                   *to_dev((inp["f_attn"], inp["f_ffn"])))
+    sync()
+    sample = torch.randperm(w.n, generator=hc_inputs.generator(11))[:48].sort().values
+    print(f"  hc={hc_} full-size block, sampled tokens {sample[:4].tolist()}...", flush=True)
+    ref = oracle.block(inp["x"][sample], pi[sample], inp["attn"], inp["ffn"], inp["f_attn"][sample],
+                       inp["f_ffn"][sample])
+    rows = lambda t: t[sample.to(t.device)].cpu()
+    for k in ("preA", "postA", "combA"):
+        check(f"hc={hc_} {k} (sampled)", rows(got[k]), ref[k], TOL_F32, rho=1.0)
+    for k in ("yA", "x1", "yF", "x2", "preF", "postF", "combF"):
+        check(f"hc={hc_} {k} (sampled)", rows(got[k]), ref[k], TOL_BF16, rho=rho_for(k))
