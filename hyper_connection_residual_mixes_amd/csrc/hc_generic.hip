@@ -324,22 +324,37 @@ __global__ __launch_bounds__(kGBlock) void mixes_partial_kernel(const float* __r
 // bf16 streams. The products of bf16 stream values with bf16 numbers are exact
 // in fp32, so the projection runs on bf16 MFMAs once each fp32 weight is split
 // into three bf16 terms (w ~ hi + mid + lo, about 24 significant bits), each
-// multiplied and accumulated in fp32 (hi, then mid, then lo). Workgroup (tile,
-// slice): 4 waves x kBT 16-token row tiles, so that every B operand read from LDS
-// feeds kBT MFMAs and every weight fetched from L2 serves 64 kBT tokens: four row
-// tiles when there are three or more column tiles of mixes (hc >= 5), two below,
-// where the weights are few and shorter tiles give more workgroups. The hc_fn tile is split once, when it is written to LDS, into three
-// bf16 planes; the stream tile stays bf16. LDS rows hold 64 columns padded to
-// 144 bytes, so that 16 consecutive rows read at one column cover distinct
-// banks. Per 64-column tile and 32-column k-block, lane l (row r16 = l % 16,
-// k-group g = l / 16) reads 8 columns 8 g .. 8 g + 7 of its row tiles' tokens
-// (A) and of mix row r*16 + r16 in each plane (B), as the 16x16x32 bf16 MFMA
-// lays out its operands. The sum of squares is the diagonal of A times A (exact
+// multiplied and accumulated in fp32 (hi, then mid, then lo).
+//
+// Workgroup (tile, slice): 4 waves x kBT 16-token row tiles and a slice of
+// 64-channel blocks. Every B operand read from LDS feeds kBT MFMAs and every
+// weight fetched from L2 serves 64 kBT tokens: four row tiles when there are
+// three or more column tiles of mixes (hc >= 5) and no collapse, else two (few
+// weights; or the registers of the collapse).
+//
+// The slice is walked channel-major in 64-column tiles: block b of stream 0,
+// 1, ..., hc-1, then block b + 1. A tile is one contiguous stretch of both the
+// streams (x[t][j][64 b ..]) and the flattened hc_fn columns (j d + 64 b ..).
+// With the collapse fused (y given), each thread accumulates
+// y[t][e] = sum_j pre_mix[t][j] x[t][j][e] over the hc tiles of a block, in
+// ascending j with one fma per stream, and stores it rounded once after the
+// last; the streams are read once for both.
+//
+// The hc_fn tile is split once, when it is written to LDS, into three bf16
+// planes; the stream tile stays bf16. LDS rows hold 64 columns padded to 144
+// bytes, so that 16 consecutive rows read at one column cover distinct banks.
+// Per 64-column tile and 32-column k-block, lane l (row r16 = l % 16, k-group
+// g = l / 16) reads 8 columns 8 g .. 8 g + 7 of its row tiles' tokens (A) and
+// of mix row r*16 + r16 in each plane (B), as the 16x16x32 bf16 MFMA lays out
+// its operands. The sum of squares is the diagonal of A times A (exact
 // products, fp32 accumulation).
 typedef __bf16 bf16x8_g __attribute__((ext_vector_type(8)));
-__host__ __device__ constexpr int bf16_row_tiles(int R) { return R <= 2 ? 2 : 4; }   // per wave
 constexpr int kBRow = kGCols + 8;        // LDS row stride of the bf16 tiles (elements)
-__host__ __device__ constexpr int bf16_x_slots(int R) { return 64 * bf16_row_tiles(R) * kGCols / 8 / kGBlock; }
+
+__host__ __device__ constexpr int bf16_row_tiles(int R, bool pre) { return (R <= 2 || pre) ? 2 : 4; }   // per wave
+__host__ __device__ constexpr int bf16_x_slots(int R, bool pre) {
+    return 64 * bf16_row_tiles(R, pre) * kGCols / 8 / kGBlock;
+}
 
 __device__ __forceinline__ float bf16_lo_g(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi_g(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -369,31 +384,32 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff
 }
 
 // One 64-column tile in registers: stream slot p of thread tid is token row
-// tid / 8 + 32 p, columns (tid % 8) * 8 .. +8 (8 lanes cover a row's 128 bytes);
-// hc_fn slot r is row tid / 16 + 16 r, columns (tid % 16) * 4 .. +4. Each slot
-// has a resource starting at its first row and ending at the last token or mix
-// row, so that rows past either read as zero; one lane offset (the row within
-// the slot and the column) serves every slot, the tile's column is the scalar
-// offset.
-template <int R>
+// tid / 8 + 32 p, columns (tid % 8) * 8 .. +8 (8 lanes cover a row's 128 bytes),
+// with that token's collapse weight for the tile's stream; hc_fn slot r is row
+// tid / 16 + 16 r, columns (tid % 16) * 4 .. +4. Each slot has a resource
+// starting at its first row and ending at the last token or mix row, so that
+// rows past either read as zero; one lane offset (the row within the slot and
+// the column) serves every slot, the tile's column is the scalar offset.
+template <int R, bool kPre>
 struct Bf16Stage {
-    uint4 xw[bf16_x_slots(R)];
+    uint4 xw[bf16_x_slots(R, kPre)];
+    float pm[kPre ? bf16_x_slots(R, kPre) : 1];
     uint4 wv[R];
 };
 
-template <int R>
+template <int R, bool kPre>
 struct Bf16Src {
-    __amdgpu_buffer_rsrc_t x[bf16_x_slots(R)];
+    __amdgpu_buffer_rsrc_t x[bf16_x_slots(R, kPre)];
     __amdgpu_buffer_rsrc_t w[R];
     uint32_t xoff, woff;   // lane offsets (bytes)
 };
 
-template <int R>
-__device__ __forceinline__ void make_src_bf16(Bf16Src<R>& src, const uint16_t* x, const float* hc_fn, int64_t n,
-                                              int M, int64_t K, int64_t t0) {
+template <int R, bool kPre>
+__device__ __forceinline__ void make_src_bf16(Bf16Src<R, kPre>& src, const uint16_t* x, const float* hc_fn,
+                                              int64_t n, int M, int64_t K, int64_t t0) {
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int p = 0; p < bf16_x_slots(R); ++p) {
+    for (int p = 0; p < bf16_x_slots(R, kPre); ++p) {
         const int64_t row0 = t0 + 32 * p;
         src.x[p] = rsrc_g(x + row0 * K, (n - row0) * K * 2);
     }
@@ -403,23 +419,34 @@ __device__ __forceinline__ void make_src_bf16(Bf16Src<R>& src, const uint16_t* x
     src.woff = (uint32_t)((int64_t)(tid >> 4) * K * 4 + (tid & 15) * 16);
 }
 
-template <int R>
-__device__ __forceinline__ void stage_load_bf16(Bf16Stage<R>& st, const Bf16Src<R>& src, int64_t c0, int64_t c_end) {
+// Tile (block b, stream j): flattened columns j d + 64 b .. +64, channels past d read as zero.
+template <int R, bool kPre>
+__device__ __forceinline__ void stage_load_bf16(Bf16Stage<R, kPre>& st, const Bf16Src<R, kPre>& src,
+                                                const float* pre_mix, int64_t n, int hc, int64_t d, int64_t t0,
+                                                int64_t b, int j) {
     const int tid = threadIdx.x;
-    const uint32_t xo = c0 + (tid & 7) * 8 < c_end ? src.xoff : kOffMaskedG;     // K, slice bounds: multiples of 8
-    const uint32_t wo = c0 + (tid & 15) * 4 < c_end ? src.woff : kOffMaskedG;
+    const int64_t e0 = b * kGCols, c0 = (int64_t)j * d + e0;
+    const uint32_t xo = e0 + (tid & 7) * 8 < d ? src.xoff : kOffMaskedG;     // d is a multiple of 8
+    const uint32_t wo = e0 + (tid & 15) * 4 < d ? src.woff : kOffMaskedG;
 #pragma unroll
-    for (int p = 0; p < bf16_x_slots(R); ++p) st.xw[p] = bload16(src.x[p], xo, (uint32_t)(c0 * 2));
+    for (int p = 0; p < bf16_x_slots(R, kPre); ++p) st.xw[p] = bload16(src.x[p], xo, (uint32_t)(c0 * 2));
 #pragma unroll
     for (int r = 0; r < R; ++r) st.wv[r] = bload16(src.w[r], wo, (uint32_t)(c0 * 4));
+    if constexpr (kPre) {
+#pragma unroll
+        for (int p = 0; p < bf16_x_slots(R, kPre); ++p) {
+            const int64_t t = t0 + (tid >> 3) + 32 * p;
+            st.pm[p] = t < n ? pre_mix[t * hc + j] : 0.f;
+        }
+    }
 }
 
 // ws: three planes (hi, mid, lo) of 16 R rows each.
-template <int R>
-__device__ __forceinline__ void stage_store_bf16(const Bf16Stage<R>& st, uint16_t* xs, uint16_t* ws) {
+template <int R, bool kPre>
+__device__ __forceinline__ void stage_store_bf16(const Bf16Stage<R, kPre>& st, uint16_t* xs, uint16_t* ws) {
     const int tid = threadIdx.x, col = (tid & 7) * 8;
 #pragma unroll
-    for (int p = 0; p < bf16_x_slots(R); ++p)
+    for (int p = 0; p < bf16_x_slots(R, kPre); ++p)
         *reinterpret_cast<uint4*>(xs + ((tid >> 3) + 32 * p) * kBRow + col) = st.xw[p];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -434,13 +461,12 @@ __device__ __forceinline__ void stage_store_bf16(const Bf16Stage<R>& st, uint16_
     }
 }
 
-template <int R>
-__global__ __launch_bounds__(kGBlock, 2) void mixes_partial_bf16_kernel(const uint16_t* __restrict__ x,
-                                                                        const float* __restrict__ hc_fn, int64_t n,
-                                                                        int hc, int64_t d, int cols_per_split,
-                                                                        int nsplit, float* __restrict__ part,
-                                                                        int pg) {
-    constexpr int kBT = bf16_row_tiles(R), kBTok = 64 * kBT;
+template <int R, bool kPre>
+__global__ __launch_bounds__(kGBlock, 2)   // at least two waves per SIMD
+void mixes_partial_bf16_kernel(const uint16_t* __restrict__ x, const float* __restrict__ hc_fn, int64_t n, int hc,
+                               int64_t d, int blk_per_split, int nsplit, float* __restrict__ part, int pg,
+                               const float* __restrict__ pre_mix, uint16_t* __restrict__ y) {
+    constexpr int kBT = bf16_row_tiles(R, kPre), kBTok = 64 * kBT, kSlots = bf16_x_slots(R, kPre);
     __shared__ __attribute__((aligned(16))) uint16_t xs[kBTok * kBRow];
     __shared__ __attribute__((aligned(16))) uint16_t ws[3 * 16 * R * kBRow];
     const int M = (2 + hc) * hc;
@@ -448,9 +474,11 @@ __global__ __launch_bounds__(kGBlock, 2) void mixes_partial_bf16_kernel(const ui
     const int64_t tile = blockIdx.x / nsplit;
     const int slice = (int)(blockIdx.x - tile * nsplit);
     const int64_t t0 = tile * kBTok;
-    const int64_t c_begin = (int64_t)slice * cols_per_split;
-    const int64_t c_end = c_begin + cols_per_split < K ? c_begin + cols_per_split : K;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t nblk = (d + kGCols - 1) / kGCols;
+    const int64_t b_begin = (int64_t)slice * blk_per_split;
+    const int64_t b_end = b_begin + blk_per_split < nblk ? b_begin + blk_per_split : nblk;
+    const int ntiles = (int)(b_end - b_begin) * hc;   // >= hc: slices are never empty
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r16 = lane & 15, g = lane >> 4;
     floatx4_g acc[kBT][R], gram[kBT];
 #pragma unroll
@@ -459,42 +487,78 @@ __global__ __launch_bounds__(kGBlock, 2) void mixes_partial_bf16_kernel(const ui
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[T][r] = floatx4_g{0.f, 0.f, 0.f, 0.f};
     }
-    Bf16Src<R> src;
-    make_src_bf16<R>(src, x, hc_fn, n, M, K, t0);
-    Bf16Stage<R> st;
-    stage_load_bf16<R>(st, src, c_begin, c_end);
+    float yacc[kPre ? kSlots : 1][8];
+#pragma unroll
+    for (int p = 0; p < (kPre ? kSlots : 1); ++p)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) yacc[p][i] = 0.f;
+    Bf16Src<R, kPre> src;
+    make_src_bf16<R, kPre>(src, x, hc_fn, n, M, K, t0);
+    Bf16Stage<R, kPre> st;
+    stage_load_bf16<R, kPre>(st, src, pre_mix, n, hc, d, t0, b_begin, 0);
     const uint16_t* xa = xs + (w * 16 * kBT + r16) * kBRow + g * 8;
     const uint16_t* wb = ws + r16 * kBRow + g * 8;
-    for (int64_t c0 = c_begin; c0 < c_end; c0 += kGCols) {
+    int64_t b = b_begin;
+    int j = 0;
+    for (int it = 0; it < ntiles; ++it) {
         __syncthreads();   // the previous tile is consumed
-        stage_store_bf16<R>(st, xs, ws);
+        stage_store_bf16<R, kPre>(st, xs, ws);
+        if constexpr (kPre) {
+            // collapse: stream j of block b, in ascending j; stored after the last stream
+#pragma unroll
+            for (int p = 0; p < kSlots; ++p) {
+                const uint32_t u[4] = {st.xw[p].x, st.xw[p].y, st.xw[p].z, st.xw[p].w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    yacc[p][2 * q] = fmaf(st.pm[p], bf16_lo_g(u[q]), yacc[p][2 * q]);
+                    yacc[p][2 * q + 1] = fmaf(st.pm[p], bf16_hi_g(u[q]), yacc[p][2 * q + 1]);
+                }
+            }
+            if (j == hc - 1) {
+                const int64_t e = b * kGCols + (tid & 7) * 8;
+#pragma unroll
+                for (int p = 0; p < kSlots; ++p) {
+                    const int64_t t = t0 + (tid >> 3) + 32 * p;
+                    if (t < n && e < d)
+                        *reinterpret_cast<uint4*>(y + t * d + e) =
+                            make_uint4(pack2(yacc[p][0], yacc[p][1]), pack2(yacc[p][2], yacc[p][3]),
+                                       pack2(yacc[p][4], yacc[p][5]), pack2(yacc[p][6], yacc[p][7]));
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) yacc[p][i] = 0.f;
+                }
+            }
+        }
         __syncthreads();
-        if (c0 + kGCols < c_end)   // the next tile's loads run under this tile's MFMAs
-            stage_load_bf16<R>(st, src, c0 + kGCols, c_end);
+        if (++j == hc) {
+            j = 0;
+            ++b;
+        }
+        if (it + 1 < ntiles)   // the next tile's loads run under this tile's MFMAs
+            stage_load_bf16<R, kPre>(st, src, pre_mix, n, hc, d, t0, b, j);
 #pragma unroll
         for (int kb = 0; kb < kGCols / 32; ++kb) {
-            bf16x8_g a[kBT], b[2][3];
+            bf16x8_g a[kBT], bv[2][3];
 #pragma unroll
             for (int T = 0; T < kBT; ++T)
                 a[T] = *reinterpret_cast<const bf16x8_g*>(xa + T * 16 * kBRow + kb * 32);
 #pragma unroll
             for (int plane = 0; plane < 3; ++plane)
-                b[0][plane] = *reinterpret_cast<const bf16x8_g*>(wb + plane * 16 * R * kBRow + kb * 32);
+                bv[0][plane] = *reinterpret_cast<const bf16x8_g*>(wb + plane * 16 * R * kBRow + kb * 32);
             // column tile r + 1's operands are read while tile r is multiplied
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 if (r + 1 < R) {
 #pragma unroll
                     for (int plane = 0; plane < 3; ++plane)
-                        b[(r + 1) & 1][plane] = *reinterpret_cast<const bf16x8_g*>(
+                        bv[(r + 1) & 1][plane] = *reinterpret_cast<const bf16x8_g*>(
                             wb + ((r + 1) * 16 + plane * 16 * R) * kBRow + kb * 32);
                 }
 #pragma unroll
                 for (int plane = 0; plane < 3; ++plane)
 #pragma unroll
                     for (int T = 0; T < kBT; ++T)
-                        acc[T][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[T], b[r & 1][plane], acc[T][r], 0, 0,
-                                                                            0);
+                        acc[T][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[T], bv[r & 1][plane], acc[T][r], 0,
+                                                                            0, 0);
             }
 #pragma unroll
             for (int T = 0; T < kBT; ++T)
@@ -560,49 +624,52 @@ int64_t ceil_div_g(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct GenericPlan {
     int64_t tiles;
-    int cols_per_split;
+    int per_split;      // flattened columns (fp32 plan) or 64-channel blocks (bf16 plan) per slice
     int nsplit;
     int pg;             // floats per partial row: (2+hc)hc dots + the sum of squares, padded to 4
-    size_t part_bytes;
     size_t mixes_offset;  // scratch mixes after the partial rows (fused step)
     size_t total_bytes;
 };
 
-struct SplitShape {
-    int64_t tiles;
-    int cols_per_split;
-    int nsplit;
-};
-
-// Token tiles of `tok` tokens x slices of whole 64-column tiles, about two
-// workgroups per CU.
-SplitShape split_shape(int64_t n, int64_t K, int tok) {
-    SplitShape s{};
-    s.tiles = ceil_div_g(n, tok);
-    const int64_t ncols = ceil_div_g(K, kGCols);
-    int64_t ns = ceil_div_g(512, s.tiles > 0 ? s.tiles : 1);
-    if (ns > ncols) ns = ncols;
+int64_t slice_count(int64_t tiles, int64_t units) {
+    int64_t ns = ceil_div_g(512, tiles > 0 ? tiles : 1);   // about two workgroups per CU
+    if (ns > units) ns = units;
     if (ns > kGMaxSplit) ns = kGMaxSplit;
-    if (ns < 1) ns = 1;
-    s.cols_per_split = (int)(ceil_div_g(ncols, ns) * kGCols);
-    s.nsplit = (int)ceil_div_g(K, s.cols_per_split);
-    return s;
+    return ns < 1 ? 1 : ns;
 }
 
-// The workspace layout does not depend on the stream dtype: the partial rows of
-// the larger of the two plans, then the scratch mixes.
-GenericPlan plan_generic(int64_t n, int hc, int64_t d, bool bf16) {
+// fp32 streams: 64-token tiles x slices of whole 64-column tiles of the flattened axis.
+GenericPlan plan_f32(int64_t n, int hc, int64_t d) {
+    GenericPlan p{};
+    const int64_t K = (int64_t)hc * d, ncols = ceil_div_g(K, kGCols);
+    p.tiles = ceil_div_g(n, kGTok);
+    p.per_split = (int)(ceil_div_g(ncols, slice_count(p.tiles, ncols)) * kGCols);
+    p.nsplit = (int)ceil_div_g(K, p.per_split);
+    return p;
+}
+
+// bf16 streams: 64 kBT-token tiles x slices of 64-channel blocks (all streams).
+GenericPlan plan_bf16(int64_t n, int hc, int64_t d, bool pre) {
     GenericPlan p{};
     const int M = (2 + hc) * hc;
-    const int64_t K = (int64_t)hc * d;
-    const SplitShape f = split_shape(n, K, kGTok), b = split_shape(n, K, 64 * bf16_row_tiles((M + 15) / 16));
-    const SplitShape& s = bf16 ? b : f;
-    p.tiles = s.tiles;
-    p.cols_per_split = s.cols_per_split;
-    p.nsplit = s.nsplit;
+    const int64_t nblk = ceil_div_g(d, kGCols);
+    p.tiles = ceil_div_g(n, 64 * bf16_row_tiles((M + 15) / 16, pre));
+    p.per_split = (int)ceil_div_g(nblk, slice_count(p.tiles, nblk));
+    p.nsplit = (int)ceil_div_g(nblk, p.per_split);
+    return p;
+}
+
+// The workspace layout does not depend on the stream dtype or on the collapse:
+// room for the partial rows of the largest plan, then the scratch mixes.
+GenericPlan plan_generic(int64_t n, int hc, int64_t d, bool bf16, bool pre) {
+    GenericPlan p = bf16 ? plan_bf16(n, hc, d, pre) : plan_f32(n, hc, d);
+    const int M = (2 + hc) * hc;
     p.pg = (M + 1 + 3) & ~3;
-    p.part_bytes = (size_t)p.nsplit * (size_t)n * (size_t)p.pg * sizeof(float);
-    const int ns_max = f.nsplit > b.nsplit ? f.nsplit : b.nsplit;
+    int ns_max = plan_f32(n, hc, d).nsplit;
+    for (int q = 0; q < 2; ++q) {
+        const int ns = plan_bf16(n, hc, d, q == 1).nsplit;
+        if (ns > ns_max) ns_max = ns;
+    }
     p.mixes_offset = ((size_t)ns_max * (size_t)n * (size_t)p.pg * sizeof(float) + 255) & ~size_t(255);
     p.total_bytes = p.mixes_offset + (size_t)n * (size_t)M * sizeof(float);
     return p;
@@ -615,40 +682,64 @@ void launch_partial_f32(const GenericPlan& p, const void* xv, const float* hc_fn
     const dim3 grid((unsigned)(p.tiles * p.nsplit)), block(kGBlock);
     switch ((M + 15) / 16) {
         case 1: hipLaunchKernelGGL((mixes_partial_kernel<1>), grid, block, 0, stream, x, hc_fn, n, hc, d,
-                                   p.cols_per_split, p.nsplit, part, p.pg); break;
+                                   p.per_split, p.nsplit, part, p.pg); break;
         case 2: hipLaunchKernelGGL((mixes_partial_kernel<2>), grid, block, 0, stream, x, hc_fn, n, hc, d,
-                                   p.cols_per_split, p.nsplit, part, p.pg); break;
+                                   p.per_split, p.nsplit, part, p.pg); break;
         case 3: hipLaunchKernelGGL((mixes_partial_kernel<3>), grid, block, 0, stream, x, hc_fn, n, hc, d,
-                                   p.cols_per_split, p.nsplit, part, p.pg); break;
+                                   p.per_split, p.nsplit, part, p.pg); break;
         case 4: hipLaunchKernelGGL((mixes_partial_kernel<4>), grid, block, 0, stream, x, hc_fn, n, hc, d,
-                                   p.cols_per_split, p.nsplit, part, p.pg); break;
+                                   p.per_split, p.nsplit, part, p.pg); break;
         default: hipLaunchKernelGGL((mixes_partial_kernel<5>), grid, block, 0, stream, x, hc_fn, n, hc, d,
-                                    p.cols_per_split, p.nsplit, part, p.pg); break;
+                                    p.per_split, p.nsplit, part, p.pg); break;
     }
 }
 
-void launch_partial_bf16(const GenericPlan& p, const void* x, const float* hc_fn, int64_t n, int hc, int64_t d,
-                         float* part, hipStream_t stream) {
+template <bool kPre>
+void launch_partial_bf16_t(const GenericPlan& p, const uint16_t* x, const float* hc_fn, int64_t n, int hc,
+                           int64_t d, float* part, const float* pre_mix, uint16_t* y, hipStream_t stream) {
     const int M = (2 + hc) * hc;
-    const uint16_t* xb = static_cast<const uint16_t*>(x);
     const dim3 grid((unsigned)(p.tiles * p.nsplit)), block(kGBlock);
     switch ((M + 15) / 16) {
-        case 1: hipLaunchKernelGGL((mixes_partial_bf16_kernel<1>), grid, block, 0, stream, xb, hc_fn, n, hc, d,
-                                   p.cols_per_split, p.nsplit, part, p.pg); break;
-        case 2: hipLaunchKernelGGL((mixes_partial_bf16_kernel<2>), grid, block, 0, stream, xb, hc_fn, n, hc, d,
-                                   p.cols_per_split, p.nsplit, part, p.pg); break;
-        case 3: hipLaunchKernelGGL((mixes_partial_bf16_kernel<3>), grid, block, 0, stream, xb, hc_fn, n, hc, d,
-                                   p.cols_per_split, p.nsplit, part, p.pg); break;
-        case 4: hipLaunchKernelGGL((mixes_partial_bf16_kernel<4>), grid, block, 0, stream, xb, hc_fn, n, hc, d,
-                                   p.cols_per_split, p.nsplit, part, p.pg); break;
-        default: hipLaunchKernelGGL((mixes_partial_bf16_kernel<5>), grid, block, 0, stream, xb, hc_fn, n, hc, d,
-                                    p.cols_per_split, p.nsplit, part, p.pg); break;
+        case 1: hipLaunchKernelGGL((mixes_partial_bf16_kernel<1, kPre>), grid, block, 0, stream, x, hc_fn, n, hc, d,
+                                   p.per_split, p.nsplit, part, p.pg, pre_mix, y); break;
+        case 2: hipLaunchKernelGGL((mixes_partial_bf16_kernel<2, kPre>), grid, block, 0, stream, x, hc_fn, n, hc, d,
+                                   p.per_split, p.nsplit, part, p.pg, pre_mix, y); break;
+        case 3: hipLaunchKernelGGL((mixes_partial_bf16_kernel<3, kPre>), grid, block, 0, stream, x, hc_fn, n, hc, d,
+                                   p.per_split, p.nsplit, part, p.pg, pre_mix, y); break;
+        case 4: hipLaunchKernelGGL((mixes_partial_bf16_kernel<4, kPre>), grid, block, 0, stream, x, hc_fn, n, hc, d,
+                                   p.per_split, p.nsplit, part, p.pg, pre_mix, y); break;
+        default: hipLaunchKernelGGL((mixes_partial_bf16_kernel<5, kPre>), grid, block, 0, stream, x, hc_fn, n, hc,
+                                    d, p.per_split, p.nsplit, part, p.pg, pre_mix, y); break;
     }
+}
+
+// The projection's partial rows (with the collapse when y is given), then the
+// finalize into `mixes`.
+hipError_t launch_projection(const void* x, bool bf16, int64_t n, int hc, int64_t d, const float* hc_fn,
+                             float norm_eps, float* mixes, void* workspace, const float* pre_mix, void* y,
+                             hipStream_t stream) {
+    const GenericPlan p = plan_generic(n, hc, d, bf16, y != nullptr);
+    float* part = static_cast<float*>(workspace);
+    if (bf16) {
+        const uint16_t* xb = static_cast<const uint16_t*>(x);
+        if (y)
+            launch_partial_bf16_t<true>(p, xb, hc_fn, n, hc, d, part, pre_mix, static_cast<uint16_t*>(y), stream);
+        else
+            launch_partial_bf16_t<false>(p, xb, hc_fn, n, hc, d, part, nullptr, nullptr, stream);
+    } else {
+        launch_partial_f32(p, x, hc_fn, n, hc, d, part, stream);
+    }
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    hipLaunchKernelGGL(mixes_finalize_kernel, dim3((unsigned)ceil_div_g(n, kGBlock / 64)), dim3(kGBlock), 0, stream,
+                       part, p.nsplit, p.pg, n, hc, d, norm_eps, mixes);
+    return hipGetLastError();
 }
 
 }  // namespace
 
-size_t generic_workspace_bytes(int64_t n, int hc, int64_t d) { return plan_generic(n, hc, d, true).total_bytes; }
+size_t generic_workspace_bytes(int64_t n, int hc, int64_t d) {
+    return plan_generic(n, hc, d, true, true).total_bytes;
+}
 
 hipError_t launch_split_generic(const float* mixes, const float* scale, const float* base, int64_t n, int hc,
                                 int iters, float eps, float* pre, float* post, float* comb, hipStream_t stream) {
@@ -681,20 +772,14 @@ hipError_t launch_post_generic(const void* f, const void* res, bool bf16, const 
 
 hipError_t launch_mixes_generic(const void* x, bool bf16, int64_t n, int hc, int64_t d, const float* hc_fn,
                                 float norm_eps, float* mixes, void* workspace, hipStream_t stream) {
-    const GenericPlan p = plan_generic(n, hc, d, bf16);
-    float* part = static_cast<float*>(workspace);
-    if (bf16)
-        launch_partial_bf16(p, x, hc_fn, n, hc, d, part, stream);
-    else
-        launch_partial_f32(p, x, hc_fn, n, hc, d, part, stream);
-    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    hipLaunchKernelGGL(mixes_finalize_kernel, dim3((unsigned)ceil_div_g(n, kGBlock / 64)), dim3(kGBlock), 0, stream,
-                       part, p.nsplit, p.pg, n, hc, d, norm_eps, mixes);
-    return hipGetLastError();
+    return launch_projection(x, bf16, n, hc, d, hc_fn, norm_eps, mixes, workspace, nullptr, nullptr, stream);
 }
 
+// expand (if any) -> projection (with the collapse fused for bf16 streams) ->
+// finalize -> split -> collapse (fp32 streams)
 hipError_t launch_fused_generic(const GenericRequest& r, hipStream_t stream) {
-    const GenericPlan p = plan_generic(r.n, r.hc, r.d, r.bf16);
+    const bool fused_pre = r.bf16 && r.y;
+    const GenericPlan p = plan_generic(r.n, r.hc, r.d, r.bf16, fused_pre);
     const void* src = r.res;
     if (r.f_prev) {
         if (hipError_t e = launch_post_generic(r.f_prev, r.res, r.bf16, r.post_prev, r.comb_prev, r.n, r.hc, r.d,
@@ -705,15 +790,15 @@ hipError_t launch_fused_generic(const GenericRequest& r, hipStream_t stream) {
     }
     float* mixes = r.mixes ? r.mixes
                            : reinterpret_cast<float*>(static_cast<char*>(r.workspace) + p.mixes_offset);
-    if (hipError_t e = launch_mixes_generic(src, r.bf16, r.n, r.hc, r.d, r.hc_fn, r.norm_eps, mixes, r.workspace,
-                                            stream);
+    if (hipError_t e = launch_projection(src, r.bf16, r.n, r.hc, r.d, r.hc_fn, r.norm_eps, mixes, r.workspace,
+                                         fused_pre ? r.pre_mix : nullptr, fused_pre ? r.y : nullptr, stream);
         e != hipSuccess)
         return e;
     if (hipError_t e = launch_split_generic(mixes, r.scale, r.base, r.n, r.hc, r.iters, r.eps, r.pre, r.post,
                                             r.comb, stream);
         e != hipSuccess)
         return e;
-    if (r.y) return launch_pre_generic(src, r.bf16, r.pre_mix, r.n, r.hc, r.d, r.y, stream);
+    if (r.y && !fused_pre) return launch_pre_generic(src, r.bf16, r.pre_mix, r.n, r.hc, r.d, r.y, stream);
     return hipSuccess;
 }
 
