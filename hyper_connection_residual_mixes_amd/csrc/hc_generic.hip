@@ -11,7 +11,9 @@
 // Four streams take the single-pass kernels of hc_kernels.hip. Here every step is
 // a kernel of its own; the fused boundary is their composition:
 //   split_generic_kernel    a wave per token; lane j*hc + k owns comb[j][k], rows
-//                           and columns are summed with cross-lane reads.
+//                           and columns are summed with cross-lane reads
+//                           (split_butterfly_kernel: butterflies for two and
+//                           eight streams).
 //   pre_generic_kernel      collapse, one lane per (token, 8 channels), a wave
 //                           per token and 512 channels.
 //   post_generic_kernel     expand + combine, the same mapping.
@@ -127,6 +129,77 @@ __global__ __launch_bounds__(kGBlock) void split_generic_kernel(const float* __r
         pre[t * hc + lane] = sigmoid_f(m[lane] * scale[0] + base[lane]) + eps;
     else if (lane < 2 * hc)
         post[t * hc + lane - hc] = 2.0f * sigmoid_f(m[lane] * scale[1] + base[lane]);
+}
+
+// Two or eight streams: a comb row is kH aligned lanes and a column is lanes
+// k, k + kH, ..., so the sums are butterflies instead of kH cross-lane reads
+// each. Two streams: a row is a lane pair (quad swap by 1) and a column lanes k
+// and k + 2 (quad swap by 2). Eight streams: a row takes two quad swaps and a
+// half-row mirror (DPP); a column a rotation by 8 within each 16-lane row (DPP),
+// then xor shuffles by 16 and 32. Every partner pair adds the same two numbers,
+// so all lanes of a row (column) end with the same sum. Lanes past kH * kH
+// compute on row 0 and store nothing. Otherwise the same steps as
+// split_generic_kernel.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_g(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
+}
+constexpr int kDppQuad1 = 0xb1, kDppQuad2 = 0x4e, kDppHalfMirror = 0x141, kDppRor8 = 0x128;
+
+template <int kH>
+__device__ __forceinline__ float row_sum_b(float v) {
+    v += dpp_g<kDppQuad1>(v);
+    if constexpr (kH == 8) {
+        v += dpp_g<kDppQuad2>(v);
+        v += dpp_g<kDppHalfMirror>(v);
+    }
+    return v;
+}
+template <int kH>
+__device__ __forceinline__ float row_max_b(float v) {
+    v = fmaxf(v, dpp_g<kDppQuad1>(v));
+    if constexpr (kH == 8) {
+        v = fmaxf(v, dpp_g<kDppQuad2>(v));
+        v = fmaxf(v, dpp_g<kDppHalfMirror>(v));
+    }
+    return v;
+}
+template <int kH>
+__device__ __forceinline__ float col_sum_b(float v) {
+    if constexpr (kH == 2) return v + dpp_g<kDppQuad2>(v);
+    v += dpp_g<kDppRor8>(v);
+    v += __shfl_xor(v, 16);
+    return v + __shfl_xor(v, 32);
+}
+
+template <int kH>
+__global__ __launch_bounds__(kGBlock) void split_butterfly_kernel(const float* __restrict__ mixes,
+                                                                  const float* __restrict__ scale,
+                                                                  const float* __restrict__ base, int64_t n,
+                                                                  int iters, float eps, float* __restrict__ pre,
+                                                                  float* __restrict__ post,
+                                                                  float* __restrict__ comb) {
+    static_assert(kH == 2 || kH == 8, "butterflies for two or eight streams");
+    constexpr int kM = (2 + kH) * kH;
+    const int64_t t = (int64_t)blockIdx.x * (kGBlock / 64) + (threadIdx.x >> 6);
+    if (t >= n) return;   // a whole wave leaves together
+    const int lane = threadIdx.x & 63;
+    const bool cl = lane < kH * kH;
+    const float* m = mixes + t * kM;
+    const int ci = 2 * kH + (cl ? lane : lane % kH);
+    float c = m[ci] * scale[2] + base[ci];
+    c = __expf(c - row_max_b<kH>(c));
+    c = c * __builtin_amdgcn_rcpf(row_sum_b<kH>(c)) + eps;
+    c *= __builtin_amdgcn_rcpf(col_sum_b<kH>(c) + eps);
+    for (int it = 1; it < iters; ++it) {
+        c *= __builtin_amdgcn_rcpf(row_sum_b<kH>(c) + eps);
+        c *= __builtin_amdgcn_rcpf(col_sum_b<kH>(c) + eps);
+    }
+    if (cl) comb[t * kH * kH + lane] = c;
+    if (lane < kH)
+        pre[t * kH + lane] = sigmoid_f(m[lane] * scale[0] + base[lane]) + eps;
+    else if (lane < 2 * kH)
+        post[t * kH + lane - kH] = 2.0f * sigmoid_f(m[lane] * scale[1] + base[lane]);
 }
 
 // --------------------------------------------------------- collapse / expand
@@ -743,8 +816,16 @@ size_t generic_workspace_bytes(int64_t n, int hc, int64_t d) {
 
 hipError_t launch_split_generic(const float* mixes, const float* scale, const float* base, int64_t n, int hc,
                                 int iters, float eps, float* pre, float* post, float* comb, hipStream_t stream) {
-    hipLaunchKernelGGL(split_generic_kernel, dim3((unsigned)ceil_div_g(n, kGBlock / 64)), dim3(kGBlock), 0, stream,
-                       mixes, scale, base, n, hc, iters, eps, pre, post, comb);
+    const dim3 grid((unsigned)ceil_div_g(n, kGBlock / 64));
+    if (hc == 8)
+        hipLaunchKernelGGL(split_butterfly_kernel<8>, grid, dim3(kGBlock), 0, stream, mixes, scale, base, n, iters,
+                           eps, pre, post, comb);
+    else if (hc == 2)
+        hipLaunchKernelGGL(split_butterfly_kernel<2>, grid, dim3(kGBlock), 0, stream, mixes, scale, base, n, iters,
+                           eps, pre, post, comb);
+    else
+        hipLaunchKernelGGL(split_generic_kernel, grid, dim3(kGBlock), 0, stream, mixes, scale, base, n, hc, iters,
+                           eps, pre, post, comb);
     return hipGetLastError();
 }
 
