@@ -177,7 +177,8 @@ int hc_post(const void* f, const void* residual, int dtype, const float* post, c
     if (int rc = check_aliases(outs, 1, ins, 4, allowed, 1)) return rc;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (hc != kHC)
-        return hip_status(hc::launch_post_generic(f, residual, dtype == HC_BF16, post, comb, n, hc, d, out, s));
+        return hip_status(hc::launch_post_generic(f, residual, dtype == HC_BF16, post, comb, n, hc, d, out, s,
+                                                  outs[0].bytes >= (size_t)hc::kStreamOutBytes));
     return hip_status(hc::launch_post(f, residual, dtype == HC_BF16, post, comb, n, d, out, s));
 }
 

@@ -70,16 +70,27 @@ __device__ __forceinline__ void load8(const void* base, int64_t idx, float (&v)[
     }
 }
 
-// Stores eight fp32 values rounded once to the element type.
-template <bool kBf16>
+// Stores eight fp32 values rounded once to the element type; kStream: with
+// non-temporal stores (to HBM, not kept in the caches).
+typedef unsigned int u32x4_s __attribute__((ext_vector_type(4)));
+template <bool kBf16, bool kStream = false>
 __device__ __forceinline__ void store8(void* base, int64_t idx, const float (&v)[8]) {
     if constexpr (kBf16) {
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + idx) =
-            make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7]));
+        const u32x4_s w = {pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
+        u32x4_s* p = reinterpret_cast<u32x4_s*>(static_cast<uint16_t*>(base) + idx);
+        if constexpr (kStream) __builtin_nontemporal_store(w, p);
+        else *p = w;
     } else {
-        float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + idx);
-        p[0] = make_float4(v[0], v[1], v[2], v[3]);
-        p[1] = make_float4(v[4], v[5], v[6], v[7]);
+        const u32x4_s a = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+        const u32x4_s b = {__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])};
+        u32x4_s* p = reinterpret_cast<u32x4_s*>(static_cast<float*>(base) + idx);
+        if constexpr (kStream) {
+            __builtin_nontemporal_store(a, p);
+            __builtin_nontemporal_store(b, p + 1);
+        } else {
+            p[0] = a;
+            p[1] = b;
+        }
     }
 }
 
@@ -238,7 +249,7 @@ __global__ __launch_bounds__(kGBlock) void pre_generic_kernel(const void* __rest
 
 // Every stream of the lane's 8 channels is read before any is written, so the
 // output may be the residual itself.
-template <bool kBf16>
+template <bool kBf16, bool kStream>
 __global__ __launch_bounds__(kGBlock) void post_generic_kernel(const void* __restrict__ f, const void* res,
                                                                const float* __restrict__ post,
                                                                const float* __restrict__ comb, int64_t n, int hc,
@@ -264,7 +275,7 @@ __global__ __launch_bounds__(kGBlock) void post_generic_kernel(const void* __res
 #pragma unroll
             for (int c = 0; c < 8; ++c) o[c] = fmaf(cjk, rv[j][c], o[c]);
         }
-        store8<kBf16>(out, (t * hc + k) * d + e, o);
+        store8<kBf16, kStream>(out, (t * hc + k) * d + e, o);
     }
 }
 
@@ -840,14 +851,20 @@ hipError_t launch_pre_generic(const void* x, bool bf16, const float* pre_mix, in
 }
 
 hipError_t launch_post_generic(const void* f, const void* res, bool bf16, const float* post, const float* comb,
-                               int64_t n, int hc, int64_t d, void* out, hipStream_t stream) {
+                               int64_t n, int hc, int64_t d, void* out, hipStream_t stream, bool stream_out) {
     const dim3 grid((unsigned)wave_grid(n, d));
-    if (bf16)
-        hipLaunchKernelGGL(post_generic_kernel<true>, grid, dim3(kGBlock), 0, stream, f, res, post, comb, n, hc, d,
-                           out);
+    if (bf16 && stream_out)
+        hipLaunchKernelGGL((post_generic_kernel<true, true>), grid, dim3(kGBlock), 0, stream, f, res, post, comb, n,
+                           hc, d, out);
+    else if (bf16)
+        hipLaunchKernelGGL((post_generic_kernel<true, false>), grid, dim3(kGBlock), 0, stream, f, res, post, comb, n,
+                           hc, d, out);
+    else if (stream_out)
+        hipLaunchKernelGGL((post_generic_kernel<false, true>), grid, dim3(kGBlock), 0, stream, f, res, post, comb, n,
+                           hc, d, out);
     else
-        hipLaunchKernelGGL(post_generic_kernel<false>, grid, dim3(kGBlock), 0, stream, f, res, post, comb, n, hc, d,
-                           out);
+        hipLaunchKernelGGL((post_generic_kernel<false, false>), grid, dim3(kGBlock), 0, stream, f, res, post, comb,
+                           n, hc, d, out);
     return hipGetLastError();
 }
 

@@ -62,6 +62,12 @@ hipError_t launch_rmsnorm_mxfp8(const void* x, bool bf16, const float* gain, int
 // single-pass kernels above.
 constexpr int kMaxHC = 8;
 
+// Expand outputs of at least this many bytes (hc_post) are streamed to HBM with
+// non-temporal stores: a quarter of the 256 MB last-level cache and well beyond
+// the L2s, where keeping them cached would only defer their write-back into the
+// next kernel's reads.
+constexpr int64_t kStreamOutBytes = int64_t(64) << 20;
+
 struct GenericRequest {
     const void* res;         // [n][hc][d]
     const void* f_prev;      // [n][d] or null (no expand)
@@ -93,7 +99,8 @@ hipError_t launch_split_generic(const float* mixes, const float* scale, const fl
 hipError_t launch_pre_generic(const void* x, bool bf16, const float* pre_mix, int64_t n, int hc, int64_t d, void* y,
                               hipStream_t stream);
 hipError_t launch_post_generic(const void* f, const void* res, bool bf16, const float* post, const float* comb,
-                               int64_t n, int hc, int64_t d, void* out, hipStream_t stream);
+                               int64_t n, int hc, int64_t d, void* out, hipStream_t stream,
+                               bool stream_out = false);
 hipError_t launch_mixes_generic(const void* x, bool bf16, int64_t n, int hc, int64_t d, const float* hc_fn,
                                 float norm_eps, float* mixes, void* workspace, hipStream_t stream);
 hipError_t launch_fused_generic(const GenericRequest& r, hipStream_t stream);

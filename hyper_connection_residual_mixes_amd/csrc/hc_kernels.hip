@@ -288,7 +288,11 @@ __device__ __forceinline__ void expand8(const Vec8<kBf16>& f, const Vec8<kBf16> 
     }
 }
 
-template <bool kBf16>
+// kStream: the outputs are written with non-temporal stores, which go to HBM
+// without being kept in the caches. Chosen for outputs far larger than the
+// caches, where keeping them would only defer their write-back into the next
+// kernel's reads.
+template <bool kBf16, bool kStream>
 __global__ __launch_bounds__(kEwBlock) void post_kernel(const void* __restrict__ f, const void* res,
                                                         const float* __restrict__ post,
                                                         const float* __restrict__ comb, int64_t n,
@@ -312,7 +316,21 @@ __global__ __launch_bounds__(kEwBlock) void post_kernel(const void* __restrict__
     for (int j = 0; j < kHC; ++j) rv[j].load(res, (t * kHC + j) * d + e);
     expand8<kBf16>(fv, rv, pk, cm, ov);
 #pragma unroll
-    for (int k = 0; k < kHC; ++k) ov[k].store(out, (t * kHC + k) * d + e);
+    for (int k = 0; k < kHC; ++k) {
+        if constexpr (kStream && kBf16) {
+            __builtin_nontemporal_store(u32x4_t{ov[k].raw.x, ov[k].raw.y, ov[k].raw.z, ov[k].raw.w},
+                                        reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(out) + (t * kHC + k) * d + e));
+        } else if constexpr (kStream) {
+            u32x4_t* q = reinterpret_cast<u32x4_t*>(static_cast<float*>(out) + (t * kHC + k) * d + e);
+            const float* v = ov[k].v;
+            __builtin_nontemporal_store(u32x4_t{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                                __float_as_uint(v[3])}, q);
+            __builtin_nontemporal_store(u32x4_t{__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]),
+                                                __float_as_uint(v[7])}, q + 1);
+        } else {
+            ov[k].store(out, (t * kHC + k) * d + e);
+        }
+    }
 }
 
 // ------------------------------------------------------ fp32 stream pass
@@ -1396,10 +1414,16 @@ hipError_t launch_pre(const void* x, bool bf16, const float* pre_mix, int64_t n,
 hipError_t launch_post(const void* f, const void* res, bool bf16, const float* post, const float* comb,
                        int64_t n, int64_t d, void* out, hipStream_t stream) {
     const dim3 grid((unsigned)ceil_div(n * (d / 8), kEwBlock));
-    if (bf16)
-        hipLaunchKernelGGL(post_kernel<true>, grid, dim3(kEwBlock), 0, stream, f, res, post, comb, n, d, out);
+    const bool stream_out = n * kHC * d * (bf16 ? 2 : 4) >= kStreamOutBytes;
+    if (bf16 && stream_out)
+        hipLaunchKernelGGL((post_kernel<true, true>), grid, dim3(kEwBlock), 0, stream, f, res, post, comb, n, d, out);
+    else if (bf16)
+        hipLaunchKernelGGL((post_kernel<true, false>), grid, dim3(kEwBlock), 0, stream, f, res, post, comb, n, d, out);
+    else if (stream_out)
+        hipLaunchKernelGGL((post_kernel<false, true>), grid, dim3(kEwBlock), 0, stream, f, res, post, comb, n, d, out);
     else
-        hipLaunchKernelGGL(post_kernel<false>, grid, dim3(kEwBlock), 0, stream, f, res, post, comb, n, d, out);
+        hipLaunchKernelGGL((post_kernel<false, false>), grid, dim3(kEwBlock), 0, stream, f, res, post, comb, n, d,
+                           out);
     return hipGetLastError();
 }
 

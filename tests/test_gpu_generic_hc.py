@@ -175,3 +175,17 @@ def test_block_full_size_sampled(hc_):
         check(f"hc={hc_} {k} (sampled)", rows(got[k]), ref[k], TOL_F32, rho=1.0)
     for k in ("yA", "x1", "yF", "x2", "preF", "postF", "combF"):
         check(f"hc={hc_} {k} (sampled)", rows(got[k]), ref[k], TOL_BF16, rho=rho_for(k))
+
+
+@pytest.mark.parametrize("hc_,dtype,n,d", [(8, torch.bfloat16, 820, 5120), (2, torch.float32, 2049, 4096)])
+def test_post_streamed_output(hc_, dtype, n, d):
+    """64 MiB and more of expand output are written with non-temporal stores."""
+    x, f, _, post, comb = _streams_case(hc_, dtype, n, d, seed=80 + hc_)
+    tol = TOL_F32 if dtype == torch.float32 else TOL_BF16
+    xd, fd, pd, cd = to_dev((x, f, post, comb))
+    out = hc.hc_post(fd, xd, pd, cd)
+    sync()
+    check(f"hc={hc_} post {dtype} {n}x{d} (streamed)", out, oracle.hc_post(f, x, post, comb), tol)
+    hc.hc_post(fd, xd, pd, cd, out=xd)          # exact in-place
+    sync()
+    assert torch.equal(xd.cpu(), out.cpu())

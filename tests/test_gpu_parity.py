@@ -98,6 +98,14 @@ def test_post_and_in_place(dtype, n, d):
     assert torch.equal(xd.cpu(), got.cpu())
 
 
+
+# 64 MiB and more of expand output are written with non-temporal stores: fp32 and
+# bf16 just above that size, bf16 just below it (ragged against 256-lane blocks)
+@pytest.mark.parametrize("dtype,n,d", [(torch.float32, 4099, 1024), (torch.bfloat16, 1639, 5120),
+                                       (torch.bfloat16, 1638, 5120)])
+def test_post_streamed_output(dtype, n, d):
+    test_post_and_in_place(dtype, n, d)
+
 # ------------------------------------------------------------------- mixes
 @pytest.mark.parametrize("dtype,n,d", CASES)
 def test_mixes(dtype, n, d):
