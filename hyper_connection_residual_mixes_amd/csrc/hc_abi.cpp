@@ -12,6 +12,9 @@
 namespace {
 
 constexpr int kHC = 4;
+// Rows (tokens) per call: every grid dimension the launchers derive from n stays
+// far below 2^31 workgroups.
+constexpr int64_t kMaxRows = 0x7fffffff;
 
 struct Span {
     const void* p;
@@ -32,7 +35,7 @@ size_t elem_size(int dtype) { return dtype == HC_BF16 ? 2 : 4; }
 // Shape rules shared by the stream entry points. Returns HC_OK or an error.
 int check_shape(int64_t n, int hc, int64_t d, int dtype) {
     // d <= 2^20 keeps every per-wave byte offset of the kernels within 31 bits
-    if (n < 0 || d < 1 || d > (int64_t(1) << 20)) return HC_ERR_SHAPE;
+    if (n < 0 || n > kMaxRows || d < 1 || d > (int64_t(1) << 20)) return HC_ERR_SHAPE;
     if (dtype != HC_F32 && dtype != HC_BF16) return HC_ERR_UNSUPPORTED;
     if (hc < 1 || hc > hc::kMaxHC || d % 8 != 0) return HC_ERR_UNSUPPORTED;
     // every byte offset must fit comfortably in 63 bits
@@ -100,7 +103,7 @@ size_t hc_workspace_size(int64_t n, int hc, int64_t d) {
 
 int hc_split_sinkhorn(const float* mixes, const float* hc_scale, const float* hc_base, int64_t n, int hc,
                       int sinkhorn_iters, float eps, float* pre, float* post, float* comb, void* stream) {
-    if (n < 0) return HC_ERR_SHAPE;
+    if (n < 0 || n > kMaxRows) return HC_ERR_SHAPE;
     if (hc < 1 || hc > hc::kMaxHC) return HC_ERR_UNSUPPORTED;
     if (sinkhorn_iters < 1 || check_eps(eps) != HC_OK) return HC_ERR_ARG;
     if (n == 0) return HC_OK;
@@ -139,7 +142,7 @@ int hc_rmsnorm_mxfp8(const void* x, int dtype, const float* gain, int64_t n, int
                      void* y_norm, uint8_t* q, uint8_t* scale, void* stream) {
     if (n < 0 || d < 8 || d > (int64_t(1) << 20)) return HC_ERR_SHAPE;
     if (n > 0 && (uint64_t)d > (uint64_t(1) << 40) / (uint64_t)n) return HC_ERR_SHAPE;
-    if (n > 0x7fffffff) return HC_ERR_SHAPE;                     // the documented row bound
+    if (n > kMaxRows) return HC_ERR_SHAPE;                       // the documented row bound
     if (dtype != HC_F32 && dtype != HC_BF16) return HC_ERR_UNSUPPORTED;
     if (d % 8 != 0) return HC_ERR_UNSUPPORTED;
     if (check_eps(norm_eps) != HC_OK) return HC_ERR_ARG;

@@ -33,9 +33,10 @@
  *   - dtype selects the stream element type: HC_F32 or HC_BF16. Coefficients
  *     and parameters are always fp32. Arithmetic is fp32; bf16 results are
  *     rounded to nearest, ties to even.
- *   - Supported sizes: 1 <= hc <= 8; 8 <= d <= 1048576 and d % 8 == 0; n >= 0
- *     (n == 0 is a no-op returning HC_OK without touching any pointer) and
- *     n * d <= 2^40. Larger d or n * d return HC_ERR_SHAPE. hc == 4 runs the
+ *   - Supported sizes: 1 <= hc <= 8; 8 <= d <= 1048576 and d % 8 == 0;
+ *     0 <= n < 2^31 (n == 0 is a no-op returning HC_OK without touching any
+ *     pointer) and n * d <= 2^40. Larger n, d or n * d return HC_ERR_SHAPE
+ *     (hc_split_sinkhorn takes the same bound on n). hc == 4 runs the
  *     single-pass kernels; other stream counts run one kernel per step (the
  *     fused boundary as expand, projection, split, collapse in sequence).
  *   - Alignment: every tensor pointer (streams, sublayer input/output, hc_fn,
@@ -66,7 +67,7 @@ extern "C" {
 
 #define HC_OK 0
 #define HC_ERR_NULL (-1)        /* a required pointer is NULL */
-#define HC_ERR_SHAPE (-2)       /* n < 0, d < 1 or d, n * d too large */
+#define HC_ERR_SHAPE (-2)       /* n < 0, d < 1 or n, d, n * d too large */
 #define HC_ERR_UNSUPPORTED (-3) /* hc outside 1..8, d % 8 != 0, unknown dtype */
 #define HC_ERR_ALIGN (-4)       /* a pointer breaks the alignment rule */
 #define HC_ERR_ARG (-5)         /* sinkhorn_iters < 1, eps or norm_eps negative or not finite */

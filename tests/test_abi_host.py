@@ -183,6 +183,18 @@ def test_rmsnorm_mxfp8_validation():
     assert _norm(sc=0x40000000 + 16 * 256 - 8) == ALIAS  # scales inside codes
 
 
+def test_row_bound():
+    """n >= 2^31 rows is rejected by every entry point before any launch, also where
+    n * d is still within its own bound (the launch grids derive from n)."""
+    big = 1 << 31
+    assert _split(n=big) == SHAPE
+    assert _split(n=big - 1, mixes=None) == NULL          # the bound itself passes
+    assert _pre(n=big, d=8) == SHAPE
+    assert _post(n=big, d=8) == SHAPE
+    assert _mixes(n=big, d=8) == SHAPE
+    assert _fused(n=big, d=8) == SHAPE
+
+
 @pytest.mark.parametrize("fn", ["hc_pre", "hc_post", "hc_mixes", "hc_fused_step"])
 def test_huge_shapes_rejected(fn):
     if fn == "hc_pre":
