@@ -370,6 +370,13 @@ __global__ __launch_bounds__(kGBlock) void mixes_partial_kernel(const float* __r
         if (c0 + kGCols < c_end)   // the next tile's loads run under this tile's MFMAs
             stage_load<R>(st, x, hc_fn, n, M, K, t0, c0 + kGCols, c_end);
         const float* xa = xs + (w * 16 + r16) * kGRow + 16 * g;
+        // the tile's 64 products per dot (and 16 squares per lane) go to fresh
+        // accumulators, added to the running ones once per tile: accumulation chains
+        // stay one tile long, so the rounding error does not grow with the slice
+        floatx4_g tacc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) tacc[r] = floatx4_g{0.f, 0.f, 0.f, 0.f};
+        float tss = 0.f;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
             const float4 a = *reinterpret_cast<const float4*>(xa + 4 * q4);
@@ -380,14 +387,17 @@ __global__ __launch_bounds__(kGBlock) void mixes_partial_kernel(const float* __r
             const float av[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                ss = fmaf(av[e], av[e], ss);
+                tss = fmaf(av[e], av[e], tss);
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     const float bv[4] = {b[r].x, b[r].y, b[r].z, b[r].w};
-                    acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bv[e], acc[r], 0, 0, 0);
+                    tacc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bv[e], tacc[r], 0, 0, 0);
                 }
             }
         }
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] += tacc[r];
+        ss += tss;
     }
     ss += __shfl_xor(ss, 16);
     ss += __shfl_xor(ss, 32);

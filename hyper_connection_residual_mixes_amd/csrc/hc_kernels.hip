@@ -506,10 +506,12 @@ __device__ __forceinline__ void step_elementwise(const PassArgs& a, const StepDa
         yv.round();
         if (live) yv.store(a.y, t * d + e);
     }
+    float ss = 0.f;   // this step's 32 squares, added to the running sum once
 #pragma unroll
     for (int j = 0; j < kHC; ++j)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) sumsq = fmaf(xs[j].v[c], xs[j].v[c], sumsq);
+        for (int c = 0; c < 8; ++c) ss = fmaf(xs[j].v[c], xs[j].v[c], ss);
+    sumsq += ss;
 }
 
 // The sweep: workgroup = 4 waves x kTiles tiles of 16 tokens. Per 32-channel step,
@@ -574,8 +576,14 @@ __global__ __launch_bounds__(kPassBlock) void pass_kernel(PassArgs a) {
             step_elementwise<kPost, kPre>(a, in[q], co[q], t[q], tok_ok[q] && e < d, e, xs[q], sumsq[q]);
 
         {
-            // lane (r, g): A = token r, channel g*8 + c; B = mix nt*16 + r, same channel
+            // lane (r, g): A = token r, channel g*8 + c; B = mix nt*16 + r, same channel.
+            // The step's 128 products per dot go to a fresh accumulator that is added to
+            // the running one once: accumulation chains stay one step long, so the
+            // rounding error does not grow with the slice length.
             const float* W = lds.w[buf];
+            floatx4_t sacc[kTiles][2];
+#pragma unroll
+            for (int q = 0; q < kTiles; ++q) sacc[q][0] = sacc[q][1] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -588,9 +596,14 @@ __global__ __launch_bounds__(kPassBlock) void pass_kernel(PassArgs a) {
                     for (int c = 0; c < 8; ++c)
 #pragma unroll
                         for (int q = 0; q < kTiles; ++q)
-                            acc[q][nt] =
-                                __builtin_amdgcn_mfma_f32_16x16x4f32(xs[q][j].v[c], bv[c], acc[q][nt], 0, 0, 0);
+                            sacc[q][nt] =
+                                __builtin_amdgcn_mfma_f32_16x16x4f32(xs[q][j].v[c], bv[c], sacc[q][nt], 0, 0, 0);
                 }
+#pragma unroll
+            for (int q = 0; q < kTiles; ++q) {
+                acc[q][0] += sacc[q][0];
+                acc[q][1] += sacc[q][1];
+            }
         }
         // the other buffer was last read before the previous barrier
         if (more) commit_weights(lds.w[buf ^ 1], wnext);

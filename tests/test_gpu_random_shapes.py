@@ -4,8 +4,8 @@ seeded random configurations against the oracle.
 The configurations are drawn once from a fixed seed: stream counts 1..8 (four
 included, which runs the single-pass kernels), 1..300 tokens, widths d = 8k up
 to 2400 (ragged against the 64-token tiles, 64-channel steps and 64-column
-tiles), both stream dtypes and 1..25 Sinkhorn rounds. Tolerances as in the block
-tests.
+tiles), both stream dtypes and 1..25 Sinkhorn rounds; and the widest supported
+stream, d = 2^20, at a few tokens. Tolerances as in the block tests.
 """
 import random
 
@@ -36,6 +36,19 @@ def _cases(count=24, seed=2024):
 
 @pytest.mark.parametrize("hc_,n,d,dtype,iters,seed", _cases())
 def test_block_random_shape(hc_, n, d, dtype, iters, seed):
+    _block_case(hc_, n, d, dtype, iters, seed)
+
+
+# The widest supported stream, d = 2^20: the largest per-lane and per-row byte
+# offsets the kernels form (the single-pass sweeps, the fp32 pass and the generic
+# bf16 projection), a few tokens each so the oracle stays within seconds.
+@pytest.mark.parametrize("hc_,n,dtype,seed", [(4, 3, torch.bfloat16, 900), (4, 2, torch.float32, 901),
+                                              (2, 3, torch.bfloat16, 902), (2, 3, torch.float32, 903)])
+def test_block_max_width(hc_, n, dtype, seed):
+    _block_case(hc_, n, 1 << 20, dtype, 20, seed)
+
+
+def _block_case(hc_, n, d, dtype, iters, seed):
     g = hc_inputs.generator(seed)
     mode = "ones" if dtype == torch.float32 else "uniform"
     attn = hc_inputs.mix_params(g, hc_, d, mode)
