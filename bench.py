@@ -291,8 +291,11 @@ def split_stress(dev, steps: int = 20):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # The block time settles only after ~130 back-to-back steps (~27 ms of load: 216 us per
+    # step over the first 40 after a short warm-up, 201.5 us from then on), so the default
+    # warm-up runs 200 steps.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--sets", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ceiling", action="store_true")
