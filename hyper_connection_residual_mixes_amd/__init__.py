@@ -103,6 +103,17 @@ def _dev(t: torch.Tensor, what: str, dtype=None) -> torch.Tensor:
     return t
 
 
+def _size(t: torch.Tensor, count: int, what: str, device) -> torch.Tensor:
+    """The library reads or writes exactly ``count`` elements behind each pointer: a
+    tensor of another size, or on another device, is refused here rather than
+    faulting the GPU."""
+    if t.numel() != count:
+        raise ValueError(f"{what} must hold {count} elements, got {t.numel()} (shape {tuple(t.shape)})")
+    if t.device != device:
+        raise ValueError(f"{what} is on {t.device}, expected {device}")
+    return t
+
+
 def _streams_shape(x: torch.Tensor):
     if x.dim() < 2:
         raise ValueError("streams must have shape [..., hc, d]")
@@ -121,6 +132,9 @@ def _workspace(n, hc, d, device, workspace):
     """The caller's workspace (its size is checked by the library), or a new one."""
     if workspace is None:
         workspace = torch.empty(max(workspace_size(n, hc, d), 16), dtype=torch.uint8, device=device)
+    _dev(workspace, "workspace")
+    if workspace.device != device:
+        raise ValueError(f"workspace is on {workspace.device}, expected {device}")
     return workspace, workspace.numel() * workspace.element_size()
 
 
@@ -129,9 +143,11 @@ def hc_mixes(x, hc_fn, norm_eps=NORM_EPS, out=None, workspace=None):
     _dev(x, "x")
     _dev(hc_fn, "hc_fn", torch.float32)
     lead, n, hc, d = _streams_shape(x)
+    M = (2 + hc) * hc
+    _size(hc_fn, M * hc * d, "hc_fn", x.device)
     if out is None:
-        out = torch.empty(*lead, (2 + hc) * hc, dtype=torch.float32, device=x.device)
-    _dev(out, "mixes", torch.float32)
+        out = torch.empty(*lead, M, dtype=torch.float32, device=x.device)
+    _size(_dev(out, "mixes", torch.float32), n * M, "mixes", x.device)
     ws, ws_bytes = _workspace(n, hc, d, x.device, workspace)
     _check("hc_mixes", lib().hc_mixes(_ptr(x), _dtype_code(x), n, hc, d, _ptr(hc_fn), float(norm_eps),
                                       _ptr(out), _ptr(ws), ws_bytes, _stream(x.device)))
@@ -156,6 +172,12 @@ def hc_split_sinkhorn(mixes, hc_scale, hc_base, hc_mult=HC_MULT, sinkhorn_iters=
     pre, post, comb = (_dev(t, nm, torch.float32) for t, nm in zip(out, ("pre", "post", "comb")))
     if m != (2 + hc_mult) * hc_mult:
         raise ValueError(f"mixes last dim must be {(2 + hc_mult) * hc_mult}, got {m}")
+    dev = mixes.device
+    _size(hc_scale, 3, "hc_scale", dev)
+    _size(hc_base, m, "hc_base", dev)
+    _size(pre, n * hc_mult, "pre", dev)
+    _size(post, n * hc_mult, "post", dev)
+    _size(comb, n * hc_mult * hc_mult, "comb", dev)
     _check("hc_split_sinkhorn", lib().hc_split_sinkhorn(
         _ptr(mixes), _ptr(hc_scale), _ptr(hc_base), n, hc_mult, int(sinkhorn_iters), float(eps),
         _ptr(pre), _ptr(post), _ptr(comb), _stream(mixes.device)))
@@ -167,9 +189,10 @@ def hc_pre(x, pre_mix, out=None):
     _dev(x, "x")
     _dev(pre_mix, "pre_mix", torch.float32)
     lead, n, hc, d = _streams_shape(x)
+    _size(pre_mix, n * hc, "pre_mix", x.device)
     if out is None:
         out = torch.empty(*lead, d, dtype=x.dtype, device=x.device)
-    _dev(out, "y", x.dtype)
+    _size(_dev(out, "y", x.dtype), n * d, "y", x.device)
     _check("hc_pre", lib().hc_pre(_ptr(x), _dtype_code(x), _ptr(pre_mix), n, hc, d, _ptr(out),
                                   _stream(x.device)))
     return out
@@ -182,9 +205,13 @@ def hc_post(f, residual, post, comb, out=None):
     _dev(post, "post", torch.float32)
     _dev(comb, "comb", torch.float32)
     lead, n, hc, d = _streams_shape(residual)
+    dev = residual.device
+    _size(f, n * d, "f", dev)
+    _size(post, n * hc, "post", dev)
+    _size(comb, n * hc * hc, "comb", dev)
     if out is None:
         out = torch.empty_like(residual)
-    _dev(out, "out", f.dtype)
+    _size(_dev(out, "out", f.dtype), n * hc * d, "out", dev)
     _check("hc_post", lib().hc_post(_ptr(f), _ptr(residual), _dtype_code(f), _ptr(post), _ptr(comb), n,
                                     hc, d, _ptr(out), _stream(f.device)))
     return out
@@ -200,13 +227,18 @@ def rmsnorm_mxfp8(x, gain, norm_eps=NORM_EPS, want_norm=True, want_cast=True, y_
     _dev(gain, "gain", torch.float32)
     d = x.shape[-1]
     n = x.numel() // d if d else 0
+    _size(gain, d, "gain", x.device)
     if want_norm and y_norm is None:
         y_norm = torch.empty_like(x)
+    if want_norm:
+        _size(_dev(y_norm, "y_norm", x.dtype), n * d, "y_norm", x.device)
     if want_cast:
         if q is None:
             q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
         if scale is None:
             scale = torch.empty(*x.shape[:-1], d // 32, dtype=torch.uint8, device=x.device)
+        _size(_dev(q, "q", torch.uint8), n * d, "q", x.device)
+        _size(_dev(scale, "scale", torch.uint8), n * (d // 32), "scale", x.device)
     else:
         q = scale = None
     _check("hc_rmsnorm_mxfp8", lib().hc_rmsnorm_mxfp8(
@@ -227,18 +259,22 @@ def hc_fused_step(residual, hc_fn, hc_scale, hc_base, pre_mix=None, f_prev=None,
     lead, n, hc, d = _streams_shape(residual)
     dev = residual.device
     expand = f_prev is not None
+    M = (2 + hc) * hc
+    _size(_dev(hc_fn, "hc_fn", torch.float32), M * hc * d, "hc_fn", dev)
+    _size(_dev(hc_scale, "hc_scale", torch.float32), 3, "hc_scale", dev)
+    _size(_dev(hc_base, "hc_base", torch.float32), M, "hc_base", dev)
     if expand:
-        _dev(f_prev, "f_prev", residual.dtype)
-        _dev(post_prev, "post_prev", torch.float32)
-        _dev(comb_prev, "comb_prev", torch.float32)
+        _size(_dev(f_prev, "f_prev", residual.dtype), n * d, "f_prev", dev)
+        _size(_dev(post_prev, "post_prev", torch.float32), n * hc, "post_prev", dev)
+        _size(_dev(comb_prev, "comb_prev", torch.float32), n * hc * hc, "comb_prev", dev)
         if streams_out is None:
             streams_out = torch.empty_like(residual)
-        _dev(streams_out, "streams_out", residual.dtype)
+        _size(_dev(streams_out, "streams_out", residual.dtype), n * hc * d, "streams_out", dev)
     if want_y:
-        _dev(pre_mix, "pre_mix", torch.float32)
+        _size(_dev(pre_mix, "pre_mix", torch.float32), n * hc, "pre_mix", dev)
         if y is None:
             y = torch.empty(*lead, d, dtype=residual.dtype, device=dev)
-        _dev(y, "y", residual.dtype)
+        _size(_dev(y, "y", residual.dtype), n * d, "y", dev)
     else:
         y = None
     if out is None:
@@ -246,6 +282,9 @@ def hc_fused_step(residual, hc_fn, hc_scale, hc_base, pre_mix=None, f_prev=None,
                torch.empty(*lead, hc, dtype=torch.float32, device=dev),
                torch.empty(*lead, hc, hc, dtype=torch.float32, device=dev))
     pre, post, comb = out
+    _size(_dev(pre, "pre", torch.float32), n * hc, "pre", dev)
+    _size(_dev(post, "post", torch.float32), n * hc, "post", dev)
+    _size(_dev(comb, "comb", torch.float32), n * hc * hc, "comb", dev)
     mixes = torch.empty(*lead, (2 + hc) * hc, dtype=torch.float32, device=dev) if want_mixes else None
     ws, ws_bytes = _workspace(n, hc, d, dev, workspace)
     _check("hc_fused_step", lib().hc_fused_step(
