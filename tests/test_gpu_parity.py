@@ -214,6 +214,43 @@ def test_fused_deterministic_and_zero_tokens():
     assert e["pre"].numel() == 0
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_fused_degenerate_tokens(dtype):
+    """Tokens whose streams are all zero, of magnitude ~1e-30 (squares below the fp32
+    range, so the sum of squares is carried by norm_eps) and ~1e15 (squares near the
+    top of the fp32 range), next to ordinary ones, through the attention boundary
+    and an FFN boundary whose sublayer output is zero for the zero token. No NaN or
+    infinity, and coefficients, mixes and collapse match the oracle on the same
+    inputs. A zero token's mixes are exactly zero, so its coefficients are the
+    split of the base alone."""
+    inp = hc_inputs.decode(seed=3)
+    x = inp["x"].float().clone()
+    x[0] = 0.0
+    x[1] *= 1e-30
+    x[2] *= 1e15
+    x = x.to(dtype)
+    attn = tuple(t.float() for t in inp["attn"])
+    pi = oracle_pi(inp)
+    ref = oracle.fused_step(x, *attn, pre_mix=pi)
+    got = hc.hc_fused_step(*to_dev((x,)), *to_dev(attn), pre_mix=to_dev(pi), want_mixes=True)
+    f = inp["f_attn"].float().clone()
+    f[0] = 0.0
+    f = f.to(dtype)
+    ref2 = oracle.fused_step(x, *attn, pre_mix=pi, f_prev=f, post_prev=ref["post"], comb_prev=ref["comb"])
+    got2 = hc.hc_fused_step(*to_dev((x,)), *to_dev(attn), pre_mix=to_dev(pi), f_prev=to_dev(f),
+                            post_prev=to_dev(ref["post"]), comb_prev=to_dev(ref["comb"]), want_mixes=True)
+    sync()
+    for k in ("mixes", "pre", "post", "comb", "y"):
+        assert torch.isfinite(got[k].float()).all(), k
+    assert float(got["mixes"][0].abs().max()) == 0.0
+    assert float(got["y"][0].float().abs().max()) == 0.0
+    for k in ("mixes", "pre", "post", "comb"):
+        check(f"{dtype} {k}", got[k], ref[k], TOL_F32, rho=rho_for(k))
+    check(f"{dtype} y", got["y"], ref["y"], TOL_F32 if dtype == torch.float32 else TOL_BF16)
+    assert float(got2["streams"][0].float().abs().max()) == 0.0       # zero streams, zero output
+    check(f"{dtype} x1", got2["streams"], ref2["streams"], TOL_F32 if dtype == torch.float32 else TOL_BF16)
+
+
 # ------------------------------------------------------- long prefill, 40 layers
 def test_long_prefill_40_layers_sampled_tokens():
     """Long prefill (B=2, T=32768: 65,536 tokens, d=5120, bf16 streams): the 40
