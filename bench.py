@@ -27,9 +27,9 @@ sys.path.insert(0, ROOT)
 KERNEL_SOURCES = ("hyper_connection_residual_mixes_amd/csrc/hc_kernels.hip",
                   "hyper_connection_residual_mixes_amd/csrc/hc_internal.h")
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "ffn_boundary_counters_prefill_T4096.md")
-ENTRY_KERNELS = {
-    "attn_fused": "bf16_sweep_kernel<no expand, collapse> + finalize_kernel",
-    "ffn_fused": "bf16_sweep_kernel<expand, collapse> + finalize_kernel",
+ENTRY_KERNELS = {   # at the benchmark's 4096 tokens the sweeps run in 128-token groups
+    "attn_fused": "bf16_sweep2_kernel<no expand, collapse> + finalize_kernel",
+    "ffn_fused": "bf16_sweep2_kernel<expand, collapse> + finalize_kernel",
     "ffn_post": "post_kernel",
 }
 

@@ -9,9 +9,10 @@
 namespace hc {
 
 // How one sweep over n tokens x d channels is cut into workgroups: `tiles`
-// tiles of 64 tokens times `nsplit` channel slices of `chunks_per_split`
+// tiles of 64 (or 128) tokens times `nsplit` channel slices of `chunks_per_split`
 // 32-channel steps. Each (slice, token) writes one 32-float partial row.
 struct PassPlan {
+    bool wide;               // bf16: 128-token groups (bf16_sweep2_kernel)
     int64_t tiles;
     int nchunks;
     int chunks_per_split;

@@ -11,7 +11,8 @@
 //   split_kernel        one lane per token: sigmoid split + Sinkhorn in registers.
 //   pre_kernel          collapse, one lane per (token, 8 channels), 128-bit loads.
 //   post_kernel         expand + combine, one lane per (token, 8 channels).
-//   bf16_sweep_kernel   one pass over 64 tokens x a channel slice of bf16 streams:
+//   bf16_sweep_kernel   one pass over 64 tokens x a channel slice of bf16 streams
+//                       (bf16_sweep2_kernel: 128 tokens, for large n):
 //                       optional expand (previous sublayer's post/comb), optional
 //                       collapse, and the partial 24-wide projection (MFMA) and
 //                       sum of squares of the (rounded) streams, to a workspace.
@@ -877,6 +878,9 @@ constexpr int kSwBlock = kSwWaves * 64;
 constexpr int kSwTok = 64;
 constexpr int kSwASlots = kSwTok * kHC * (kStep / 8);     // 16-byte slots per A buffer (32 KB)
 constexpr int kSweepTargetGroups = 256;   // one workgroup per CU
+// From this many tokens on the bf16 sweep takes 128-token groups (bf16_sweep2_kernel);
+// below it, 128-token groups would leave lanes idle (decode: 64 tokens).
+constexpr int64_t kWideSweepTokens = 1024;
 
 struct SweepLds {
     uint4 a[2][kSwASlots];                 // 64 KB; reused for the cross-wave reduction
@@ -1101,6 +1105,249 @@ __global__ __launch_bounds__(kSwBlock) void bf16_sweep_kernel(PassArgs a) {
 #pragma unroll
             for (int w = 0; w < kSwWaves; ++w) s += lds.ss[w][T][row];
             part[t * kPart + kMix] = s;
+        }
+    }
+}
+
+// ------------------------------------------------ bf16 sweep, 128-token groups
+// The same data flow as bf16_sweep_kernel with 128 tokens per workgroup, so that
+// every weight fetched from L2 serves 128 tokens (half the L2 weight traffic per
+// token); used from kWideSweepTokens tokens on. Lane (t8, c8) of wave w owns
+// tokens 8w + t8 and 64 + 8w + t8 (8 channels per step each). To fit the
+// registers: the per-token coefficients stay in LDS, the streams are prefetched
+// one step ahead (one step of 128 tokens: the same bytes in flight as two steps
+// of 64), and the sum of squares is taken on the VALU from the (rounded) stream
+// values, summed over a token row's 8 lanes in a fixed order, instead of an MFMA
+// Gram diagonal.
+constexpr int kS2Tok = 2 * kSwTok;
+constexpr int kS2ASlots = kS2Tok * kHC * (kStep / 8);     // 64 KB per A buffer
+constexpr int kS2Coef = 6;                                // float4: post, comb rows 0..3, pre_mix
+
+struct Sweep2Lds {
+    uint4 a[2][kS2ASlots];                 // 128 KB; reused for the cross-wave reduction
+    float4 coef[kS2Tok][kS2Coef];          // 12 KB
+};
+
+template <bool kPost>
+struct StepRegs2 {
+    uint4 x[2][kHC];
+    uint4 f[2];
+};
+
+template <bool kPost, bool kPre>
+__global__ __launch_bounds__(kSwBlock) void bf16_sweep2_kernel(PassArgs a) {
+    __shared__ Sweep2Lds lds;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int mj = wave & 3, mkk = wave >> 2;
+    const int t8 = lane >> 3, c8 = lane & 7;
+    const int64_t n = a.n, d = a.d;
+    const int nkb = a.nchunks;
+    const int split = (int)(blockIdx.x % (unsigned)a.nsplit);
+    const int64_t group = blockIdx.x / (unsigned)a.nsplit;
+    const int64_t tok0 = group * kS2Tok;
+    const int tlh[2] = {wave * 8 + t8, kSwTok + wave * 8 + t8};
+    const int kb_begin = split * a.chunks_per_split;
+    const int kb_end = min(nkb, kb_begin + a.chunks_per_split);
+    const int64_t c_begin = (int64_t)kb_begin * kChunk;
+    const int64_t c_end = min(d, (int64_t)kb_end * kChunk);
+    const int nst = (int)((c_end - c_begin + kStep - 1) / kStep);
+
+    for (int i = threadIdx.x; i < kS2Tok * kS2Coef; i += kSwBlock) {
+        const int t = i / kS2Coef, q = i - t * kS2Coef;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (tok0 + t < n) {
+            if (kPost && q == 0) v = reinterpret_cast<const float4*>(a.post_prev)[tok0 + t];
+            if (kPost && q >= 1 && q <= 4) v = reinterpret_cast<const float4*>(a.comb_prev)[(tok0 + t) * kHC + q - 1];
+            if (kPre && q == 5) v = reinterpret_cast<const float4*>(a.pre_mix)[tok0 + t];
+        }
+        lds.coef[t][q] = v;
+    }
+
+    const int64_t row_x = kHC * d * 2, row_f = d * 2;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(static_cast<const char*>(a.res) + tok0 * row_x, (n - tok0) * row_x);
+    const __amdgpu_buffer_rsrc_t rf = make_rsrc(kPost ? static_cast<const char*>(a.f) + tok0 * row_f : nullptr,
+                                                kPost ? (n - tok0) * row_f : 0);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(kPost ? static_cast<char*>(a.streams_out) + tok0 * row_x : nullptr,
+                                                kPost ? (n - tok0) * row_x : 0);
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(kPre ? static_cast<char*>(a.y) + tok0 * row_f : nullptr,
+                                                kPre ? (n - tok0) * row_f : 0);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.hc_fn, (int64_t)kMix * kHC * d * 4);
+    uint32_t lane_x[2], lane_f[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const bool ok = tok0 + tlh[h] < n;
+        lane_x[h] = ok ? (uint32_t)(tlh[h] * row_x + c8 * 16) : kOffMasked;
+        lane_f[h] = ok ? (uint32_t)(tlh[h] * row_f + c8 * 16) : kOffMasked;
+    }
+    const int g = lane >> 4, col = lane & 15;
+    const uint32_t lane_w0 = (uint32_t)(((int64_t)col * kHC * d + (int64_t)mj * d + g * 8) * 4);
+    const uint32_t lane_w1 = (uint32_t)(((int64_t)(16 + (col & 7)) * kHC * d + (int64_t)mj * d + g * 8) * 4);
+
+    auto load_step = [&](StepRegs2<kPost>& R, int s) {
+        const int64_t cs = c_begin + (int64_t)s * kStep;
+        const bool ok = cs + c8 * 8 < c_end;
+        const uint32_t so = (uint32_t)(cs * 2);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t vx = ok ? lane_x[h] : kOffMasked, vf = ok ? lane_f[h] : kOffMasked;
+#pragma unroll
+            for (int j = 0; j < kHC; ++j) R.x[h][j] = buf_load16(rx, vx, so + (uint32_t)(j * row_f));
+            if constexpr (kPost) R.f[h] = buf_load16(rf, vf, so);
+        }
+    };
+    auto load_b = [&](float4 (&W)[4], int s) {
+        const int kb = kb_begin + s * kStepKb + mkk;
+        const bool ok = kb < kb_end && (int64_t)kb * kChunk + g * 8 < d;
+        const uint32_t v0 = ok ? lane_w0 : kOffMasked, v1 = ok ? lane_w1 : kOffMasked;
+        const uint32_t so = (uint32_t)(kb * kChunk * 4);
+        W[0] = buf_load16f(rw, v0, so);
+        W[1] = buf_load16f(rw, v0 + 16u, so);
+        W[2] = buf_load16f(rw, v1, so);
+        W[3] = buf_load16f(rw, v1 + 16u, so);
+    };
+
+    floatx4_t acc[8][2];
+#pragma unroll
+    for (int T = 0; T < 8; ++T) acc[T][0] = acc[T][1] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    float ssq[2] = {0.f, 0.f};
+
+    auto step = [&](int s, StepRegs2<kPost>& cur, StepRegs2<kPost>& ahead, float4 (&Wcur)[4], float4 (&Wnext)[4]) {
+        load_b(Wnext, s + 1);
+        load_step(ahead, s + 1);
+        const int64_t cs = c_begin + (int64_t)s * kStep;
+        const bool ok = cs + c8 * 8 < c_end;
+        const uint32_t so = (uint32_t)(cs * 2);
+        uint4* A = lds.a[s & 1];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int tl = tlh[h];
+            const uint32_t vx = ok ? lane_x[h] : kOffMasked, vf = ok ? lane_f[h] : kOffMasked;
+            float pk[kHC], cm[kHC * kHC], pim[kHC];
+            if constexpr (kPost) {
+                const float4 pv = lds.coef[tl][0];
+                pk[0] = pv.x; pk[1] = pv.y; pk[2] = pv.z; pk[3] = pv.w;
+#pragma unroll
+                for (int j = 0; j < kHC; ++j) {
+                    const float4 cv = lds.coef[tl][1 + j];
+                    cm[4 * j] = cv.x; cm[4 * j + 1] = cv.y; cm[4 * j + 2] = cv.z; cm[4 * j + 3] = cv.w;
+                }
+            }
+            if constexpr (kPre) {
+                const float4 pv = lds.coef[tl][5];
+                pim[0] = pv.x; pim[1] = pv.y; pim[2] = pv.z; pim[3] = pv.w;
+            }
+            uint32_t yw[4];
+            float sq = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                uint32_t xw[kHC];
+#pragma unroll
+                for (int j = 0; j < kHC; ++j) xw[j] = (&cur.x[h][j].x)[w];
+                if constexpr (kPost) {
+                    const uint32_t fw = (&cur.f[h].x)[w];
+                    const float f0 = bf16_lo(fw), f1 = bf16_hi(fw);
+                    uint32_t ow[kHC];
+#pragma unroll
+                    for (int k = 0; k < kHC; ++k) {
+                        float o0 = pk[k] * f0, o1 = pk[k] * f1;
+#pragma unroll
+                        for (int j = 0; j < kHC; ++j) {
+                            o0 = fmaf(cm[4 * j + k], bf16_lo(xw[j]), o0);
+                            o1 = fmaf(cm[4 * j + k], bf16_hi(xw[j]), o1);
+                        }
+                        ow[k] = pack_bf16x2(o0, o1);
+                    }
+#pragma unroll
+                    for (int k = 0; k < kHC; ++k) xw[k] = (&cur.x[h][k].x)[w] = ow[k];
+                }
+                float y0 = 0.f, y1 = 0.f;
+#pragma unroll
+                for (int j = 0; j < kHC; ++j) {
+                    const float a0 = bf16_lo(xw[j]), a1 = bf16_hi(xw[j]);
+                    sq = fmaf(a0, a0, sq);
+                    sq = fmaf(a1, a1, sq);
+                    if constexpr (kPre) {
+                        y0 = fmaf(pim[j], a0, y0);
+                        y1 = fmaf(pim[j], a1, y1);
+                    }
+                }
+                if constexpr (kPre) yw[w] = pack_bf16x2(y0, y1);
+            }
+            ssq[h] += sq;
+            if constexpr (kPost) {
+#pragma unroll
+                for (int k = 0; k < kHC; ++k) buf_store16(cur.x[h][k], ro, vx, so + (uint32_t)(k * row_f));
+            }
+            if constexpr (kPre) buf_store16(make_uint4(yw[0], yw[1], yw[2], yw[3]), ry, vf, so);
+#pragma unroll
+            for (int j = 0; j < kHC; ++j) A[a_slot(tl, j, c8)] = cur.x[h][j];
+        }
+        __syncthreads();
+        uint4 Bcur[kFragsPerKb], hi1, mid1, lo1;
+        split3(Wcur[0], Wcur[1], Bcur[0], Bcur[1], Bcur[2]);
+        split3(Wcur[2], Wcur[3], hi1, mid1, lo1);
+        const bool lo_half = col < 8;
+        Bcur[3] = make_uint4(lo_half ? hi1.x : mid1.x, lo_half ? hi1.y : mid1.y, lo_half ? hi1.z : mid1.z,
+                             lo_half ? hi1.w : mid1.w);
+        Bcur[4] = make_uint4(lo_half ? lo1.x : 0u, lo_half ? lo1.y : 0u, lo_half ? lo1.z : 0u, lo_half ? lo1.w : 0u);
+#pragma unroll
+        for (int T = 0; T < 8; ++T) {
+            const bf16x8_t Av =
+                __builtin_bit_cast(bf16x8_t, A[a_slot(T * 16 + (lane & 15), mj, mkk * 4 + (lane >> 4))]);
+#pragma unroll
+            for (int q = 0; q < kFragsPerKb; ++q)
+                acc[T][q < 3 ? 0 : 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    Av, __builtin_bit_cast(bf16x8_t, Bcur[q]), acc[T][q < 3 ? 0 : 1], 0, 0, 0);
+        }
+    };
+
+    StepRegs2<kPost> R0, R1;
+    float4 B0[4], B1[4];
+    load_b(B0, 0);
+    load_step(R0, 0);
+    __syncthreads();   // the coefficients are in LDS
+    int s = 0;
+    for (; s + 2 <= nst; s += 2) {
+        step(s, R0, R1, B0, B1);
+        step(s + 1, R1, R0, B1, B0);
+    }
+    if (s < nst) step(s, R0, R1, B0, B1);
+
+    __syncthreads();   // every wave is done with the A buffers
+#pragma unroll
+    for (int T = 0; T < 8; ++T)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) acc[T][1][ii] += dpp<kRowRor8>(acc[T][1][ii]);
+    float* red = reinterpret_cast<float*>(&lds.a[0][0]);   // [wave][T][nt][ii][lane], 128 KB
+#pragma unroll
+    for (int T = 0; T < 8; ++T)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) red[(((wave * 8 + T) * 2 + nt) * 4 + ii) * 64 + lane] = acc[T][nt][ii];
+    float* part = a.part + (int64_t)split * n * kPart;
+    // sum of squares: the 8 lanes of a token row (xor 1, 2, 4), in a fixed order
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float v = ssq[h];
+        v += __shfl_xor(v, 1);
+        v += __shfl_xor(v, 2);
+        v += __shfl_xor(v, 4);
+        const int64_t t = tok0 + tlh[h];
+        if (c8 == 0 && t < n) part[t * kPart + kMix] = v;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 8 * 2 * 4 * 64; e += kSwBlock) {
+        const int l = e & 63, ii = (e >> 6) & 3, nt = (e >> 8) & 1, T = e >> 9;
+        const int mix = nt * 16 + (l & 15);
+        const int64_t t = tok0 + T * 16 + 4 * (l >> 4) + ii;
+        if (mix < kMix && t < n) {
+            float sum = 0.f;
+#pragma unroll
+            for (int w = 0; w < kSwWaves; ++w) sum += red[w * 4096 + e];
+            part[t * kPart + mix] = sum;
         }
     }
 }
@@ -1383,9 +1630,11 @@ constexpr int kF32Unit = 128;   // pass_kernel slices are whole 128-channel unit
 
 PassPlan plan_pass(int64_t n, int64_t d, bool bf16) {
     PassPlan p{};
-    // bf16 sweep: 64-token groups, slices of whole 64-channel steps, ~256
-    // workgroups (one per CU); fp32 pass_kernel: 64-token tiles, 128-channel units
-    const int tok = bf16 ? kSwTok : kTokWG;
+    // bf16 sweep: 64-token groups (128 from kWideSweepTokens tokens on), slices of
+    // whole 64-channel steps, ~256 workgroups (one per CU); fp32 pass_kernel:
+    // 64-token tiles, 128-channel units
+    p.wide = bf16 && n >= kWideSweepTokens;
+    const int tok = bf16 ? (p.wide ? kS2Tok : kSwTok) : kTokWG;
     const int unit = bf16 ? kStep : kF32Unit;
     p.tiles = ceil_div(n, tok);
     p.nchunks = (int)ceil_div(d, kChunk);
@@ -1443,8 +1692,12 @@ hipError_t launch_post(const void* f, const void* res, bool bf16, const float* p
 namespace {
 template <bool kPost, bool kPre>
 void launch_sweep_t(const PassArgs& a, const PassPlan& p, hipStream_t stream) {
-    hipLaunchKernelGGL((bf16_sweep_kernel<kPost, kPre>), dim3((unsigned)(p.tiles * p.nsplit)), dim3(kSwBlock), 0,
-                       stream, a);
+    if (p.wide)
+        hipLaunchKernelGGL((bf16_sweep2_kernel<kPost, kPre>), dim3((unsigned)(p.tiles * p.nsplit)), dim3(kSwBlock),
+                           0, stream, a);
+    else
+        hipLaunchKernelGGL((bf16_sweep_kernel<kPost, kPre>), dim3((unsigned)(p.tiles * p.nsplit)), dim3(kSwBlock),
+                           0, stream, a);
 }
 
 template <bool kPost, bool kPre>

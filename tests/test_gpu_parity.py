@@ -156,6 +156,33 @@ def test_block_bf16_full(which):
     assert ref["x2"].dtype == torch.bfloat16
 
 
+@pytest.mark.parametrize("n,d", [(1031, 1288), (1024, 64)])
+def test_wide_sweep_ragged(n, d):
+    """From 1024 tokens on, the bf16 boundaries run in 128-token groups. Ragged token
+    counts and widths (a partial last group, a partial last 64-channel step, a single
+    step) through all four variants of that sweep: the block (collapse without and
+    with expand), the projection alone, and an expand without collapse."""
+    w = hc_inputs.Workload(f"wide_{n}x{d}", 1, n, d, torch.bfloat16)
+    inp = hc_inputs.block_inputs(w, seed=11, outlier_frac=0.02)
+    _block_check(inp, TOL_BF16, TOL_BF16)
+    x, fn = inp["x"], inp["attn"][0]
+    ws = torch.full((hc.workspace_size(n, 4, d),), 255, dtype=torch.uint8, device=DEV)  # NaN bytes
+    got = hc.hc_mixes(*to_dev((x, fn)), workspace=ws)
+    sync()
+    check(f"mixes {n}x{d}", got, oracle.hc_mixes(x, fn), TOL_F32)
+    pi = oracle_pi(inp)
+    a = oracle.fused_step(x, *inp["attn"], pre_mix=pi)
+    ref = oracle.fused_step(x, *inp["ffn"], pre_mix=pi, f_prev=inp["f_attn"], post_prev=a["post"],
+                            comb_prev=a["comb"])
+    got = hc.hc_fused_step(*to_dev((x,)), *to_dev(inp["ffn"]), f_prev=to_dev(inp["f_attn"]),
+                           post_prev=to_dev(a["post"]), comb_prev=to_dev(a["comb"]), want_y=False)
+    sync()
+    assert got["y"] is None
+    check(f"x1 {n}x{d}", got["streams"], ref["streams"], TOL_BF16)
+    for k in ("pre", "post", "comb"):
+        check(f"{k} {n}x{d}", got[k], ref[k], TOL_BF16, rho=1.0)
+
+
 @pytest.mark.parametrize("which", ["tiny", "decode", "prefill"])
 def test_fused_coefficients_exact_inputs(which):
     """hc_fused_step without the expand step, on streams both sides receive exactly
