@@ -4,8 +4,8 @@ seeded random configurations against the oracle.
 The configurations are drawn once from a fixed seed: stream counts 1..8 (four
 included, which runs the single-pass kernels), 1..300 tokens, widths d = 8k up
 to 2400 (ragged against the 64-token tiles, 64-channel steps and 64-column
-tiles), both stream dtypes and 1..25 Sinkhorn rounds; and the widest supported
-stream, d = 2^20, at a few tokens. Tolerances as in the block tests.
+tiles), both stream dtypes and 1..25 Sinkhorn rounds; four random bf16 blocks of 1024..3000 tokens (the
+128-token sweep); and the widest supported stream, d = 2^20, at a few tokens. Tolerances as in the block tests.
 """
 import random
 
@@ -37,6 +37,18 @@ def _cases(count=24, seed=2024):
 @pytest.mark.parametrize("hc_,n,d,dtype,iters,seed", _cases())
 def test_block_random_shape(hc_, n, d, dtype, iters, seed):
     _block_case(hc_, n, d, dtype, iters, seed)
+
+
+def _wide_cases(count=4, seed=77):
+    rng = random.Random(seed)
+    return [(rng.randint(1024, 3000), 8 * rng.randint(1, 300), 200 + i) for i in range(count)]
+
+
+# Four bf16 streams from 1024 tokens on run the 128-token sweep: seeded random token
+# counts (ragged against 128) and widths (ragged against 64-channel steps).
+@pytest.mark.parametrize("n,d,seed", _wide_cases())
+def test_block_random_wide_sweep(n, d, seed):
+    _block_case(4, n, d, torch.bfloat16, 20, seed)
 
 
 # The widest supported stream, d = 2^20: the largest per-lane and per-row byte
