@@ -1,8 +1,10 @@
-"""HIP-graph capture of the entry points: a captured decode block (attention
-boundary, FFN boundary, FFN expand; 64 tokens x 4 x 5120 bf16) replays to exactly
-the eager results, replay after replay, with eager work and synchronisations in
-between (the library records no memsets, allocations or host syncs). The eager
-block itself is checked against the oracle by the block parity tests.
+"""HIP-graph capture of the entry points: a captured block (attention boundary, FFN
+boundary, FFN expand) replays to exactly the eager results, replay after replay,
+with eager work and synchronisations in between (the library records no memsets,
+allocations or host syncs). Decode size (64 tokens x 4 x 5120 bf16: 64-token
+sweeps) and a ragged prefill-like size (1031 tokens x 4 x 1288 bf16: 128-token
+sweeps). The eager block itself is checked against the oracle by the block parity
+tests.
 """
 import pytest
 import torch
@@ -14,10 +16,11 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 
-def test_decode_block_graph_replays_match_eager():
-    w = hc_inputs.DECODE
+@pytest.mark.parametrize("w", [hc_inputs.DECODE, hc_inputs.Workload("graph_1031x1288", 1, 1031, 1288,
+                                                                    torch.bfloat16)], ids=["decode", "wide"])
+def test_block_graph_replays_match_eager(w):
     n, d = w.n, w.d
-    inp = hc_inputs.decode(seed=4, device=DEV)
+    inp = hc_inputs.block_inputs(w, seed=4, device=DEV)
     pi, _, _ = hc.hc_split_sinkhorn(*inp["prev"])
     ws = torch.empty(hc.workspace_size(n, 4, d), dtype=torch.uint8, device=DEV)
     o = dict(yA=torch.empty(n, d, dtype=w.dtype, device=DEV), yF=torch.empty(n, d, dtype=w.dtype, device=DEV),
