@@ -109,22 +109,21 @@ __device__ __forceinline__ float col_sum_g(float c, int k, int hc) {
     return s;
 }
 
-__global__ __launch_bounds__(kGBlock) void split_generic_kernel(const float* __restrict__ mixes,
-                                                                const float* __restrict__ scale,
-                                                                const float* __restrict__ base, int64_t n,
-                                                                int hc, int iters, float eps,
-                                                                float* __restrict__ pre, float* __restrict__ post,
-                                                                float* __restrict__ comb) {
-    const int64_t t = (int64_t)blockIdx.x * (kGBlock / 64) + (threadIdx.x >> 6);
-    if (t >= n) return;   // a whole wave leaves together
+// The split of one token by one wave. mix(i) returns the token's mix i; every
+// lane of the wave calls it (it may read other lanes' registers).
+template <class Mix>
+__device__ __forceinline__ void split_generic_wave(const Mix& mix, const float* __restrict__ scale,
+                                                   const float* __restrict__ base, int64_t t, int hc, int iters,
+                                                   float eps, float* __restrict__ pre, float* __restrict__ post,
+                                                   float* __restrict__ comb) {
     const int lane = threadIdx.x & 63;
-    const int M = (2 + hc) * hc, hc2 = hc * hc;
-    const float* m = mixes + t * M;
+    const int hc2 = hc * hc;
     const bool cl = lane < hc2;
     const int j = cl ? lane / hc : 0;
     const int k = cl ? lane - j * hc : 0;
     const int ci = 2 * hc + (cl ? lane : 0);
-    float c = m[ci] * scale[2] + base[ci];
+    const float mp = mix(lane < 2 * hc ? lane : 0);   // pre / post logit of lanes 0 .. 2 hc - 1
+    float c = mix(ci) * scale[2] + base[ci];
     // row softmax (max subtracted), + eps; then the column step
     float mx = -INFINITY;
     for (int kk = 0; kk < hc; ++kk) mx = fmaxf(mx, __shfl(c, j * hc + kk));
@@ -137,9 +136,21 @@ __global__ __launch_bounds__(kGBlock) void split_generic_kernel(const float* __r
     }
     if (cl) comb[t * hc2 + lane] = c;
     if (lane < hc)
-        pre[t * hc + lane] = sigmoid_f(m[lane] * scale[0] + base[lane]) + eps;
+        pre[t * hc + lane] = sigmoid_f(mp * scale[0] + base[lane]) + eps;
     else if (lane < 2 * hc)
-        post[t * hc + lane - hc] = 2.0f * sigmoid_f(m[lane] * scale[1] + base[lane]);
+        post[t * hc + lane - hc] = 2.0f * sigmoid_f(mp * scale[1] + base[lane]);
+}
+
+__global__ __launch_bounds__(kGBlock) void split_generic_kernel(const float* __restrict__ mixes,
+                                                                const float* __restrict__ scale,
+                                                                const float* __restrict__ base, int64_t n,
+                                                                int hc, int iters, float eps,
+                                                                float* __restrict__ pre, float* __restrict__ post,
+                                                                float* __restrict__ comb) {
+    const int64_t t = (int64_t)blockIdx.x * (kGBlock / 64) + (threadIdx.x >> 6);
+    if (t >= n) return;   // a whole wave leaves together
+    const float* m = mixes + t * (2 + hc) * hc;
+    split_generic_wave([&](int i) { return m[i]; }, scale, base, t, hc, iters, eps, pre, post, comb);
 }
 
 // Two or eight streams: a comb row is kH aligned lanes and a column is lanes
@@ -183,22 +194,17 @@ __device__ __forceinline__ float col_sum_b(float v) {
     return v + __shfl_xor(v, 32);
 }
 
-template <int kH>
-__global__ __launch_bounds__(kGBlock) void split_butterfly_kernel(const float* __restrict__ mixes,
-                                                                  const float* __restrict__ scale,
-                                                                  const float* __restrict__ base, int64_t n,
-                                                                  int iters, float eps, float* __restrict__ pre,
-                                                                  float* __restrict__ post,
-                                                                  float* __restrict__ comb) {
+template <int kH, class Mix>
+__device__ __forceinline__ void split_butterfly_wave(const Mix& mix, const float* __restrict__ scale,
+                                                     const float* __restrict__ base, int64_t t, int iters, float eps,
+                                                     float* __restrict__ pre, float* __restrict__ post,
+                                                     float* __restrict__ comb) {
     static_assert(kH == 2 || kH == 8, "butterflies for two or eight streams");
-    constexpr int kM = (2 + kH) * kH;
-    const int64_t t = (int64_t)blockIdx.x * (kGBlock / 64) + (threadIdx.x >> 6);
-    if (t >= n) return;   // a whole wave leaves together
     const int lane = threadIdx.x & 63;
     const bool cl = lane < kH * kH;
-    const float* m = mixes + t * kM;
     const int ci = 2 * kH + (cl ? lane : lane % kH);
-    float c = m[ci] * scale[2] + base[ci];
+    const float mp = mix(lane < 2 * kH ? lane : 0);   // pre / post logit of lanes 0 .. 2 kH - 1
+    float c = mix(ci) * scale[2] + base[ci];
     c = __expf(c - row_max_b<kH>(c));
     c = c * __builtin_amdgcn_rcpf(row_sum_b<kH>(c)) + eps;
     c *= __builtin_amdgcn_rcpf(col_sum_b<kH>(c) + eps);
@@ -208,9 +214,22 @@ __global__ __launch_bounds__(kGBlock) void split_butterfly_kernel(const float* _
     }
     if (cl) comb[t * kH * kH + lane] = c;
     if (lane < kH)
-        pre[t * kH + lane] = sigmoid_f(m[lane] * scale[0] + base[lane]) + eps;
+        pre[t * kH + lane] = sigmoid_f(mp * scale[0] + base[lane]) + eps;
     else if (lane < 2 * kH)
-        post[t * kH + lane - kH] = 2.0f * sigmoid_f(m[lane] * scale[1] + base[lane]);
+        post[t * kH + lane - kH] = 2.0f * sigmoid_f(mp * scale[1] + base[lane]);
+}
+
+template <int kH>
+__global__ __launch_bounds__(kGBlock) void split_butterfly_kernel(const float* __restrict__ mixes,
+                                                                  const float* __restrict__ scale,
+                                                                  const float* __restrict__ base, int64_t n,
+                                                                  int iters, float eps, float* __restrict__ pre,
+                                                                  float* __restrict__ post,
+                                                                  float* __restrict__ comb) {
+    const int64_t t = (int64_t)blockIdx.x * (kGBlock / 64) + (threadIdx.x >> 6);
+    if (t >= n) return;   // a whole wave leaves together
+    const float* m = mixes + t * (2 + kH) * kH;
+    split_butterfly_wave<kH>([&](int i) { return m[i]; }, scale, base, t, iters, eps, pre, post, comb);
 }
 
 // --------------------------------------------------------- collapse / expand
@@ -682,11 +701,11 @@ void mixes_partial_bf16_kernel(const uint16_t* __restrict__ x, const float* __re
 
 // A wave per token: lane l sums entries l and l + 64 of the partial rows over the
 // slices in order, then scales the dots by 1 / sqrt(sum of squares / (hc d) + eps).
-__global__ __launch_bounds__(kGBlock) void mixes_finalize_kernel(const float* __restrict__ part, int nsplit,
-                                                                 int pg, int64_t n, int hc, int64_t d,
-                                                                 float norm_eps, float* __restrict__ mixes) {
-    const int64_t t = (int64_t)blockIdx.x * (kGBlock / 64) + (threadIdx.x >> 6);
-    if (t >= n) return;   // a whole wave leaves together
+// Token t's mixes from its partial rows: lane l gets mixes l (a0) and l + 64 (a1),
+// already scaled; stores them when `mixes` is not null.
+__device__ __forceinline__ void finalize_mixes_wave(const float* __restrict__ part, int nsplit, int pg, int64_t n,
+                                                    int hc, int64_t d, float norm_eps, float* __restrict__ mixes,
+                                                    int64_t t, float& m0, float& m1) {
     const int lane = threadIdx.x & 63;
     const int M = (2 + hc) * hc;
     const int i0 = lane, i1 = lane + 64;
@@ -710,8 +729,44 @@ __global__ __launch_bounds__(kGBlock) void mixes_finalize_kernel(const float* __
     }
     const float ss = M < 64 ? __shfl(a0, M) : __shfl(a1, M - 64);
     const float rstd = 1.0f / sqrtf(ss / (float)((int64_t)hc * d) + norm_eps);
-    if (i0 < M) mixes[t * M + i0] = a0 * rstd;
-    if (i1 < M) mixes[t * M + i1] = a1 * rstd;
+    m0 = a0 * rstd;
+    m1 = a1 * rstd;
+    if (mixes && i0 < M) mixes[t * M + i0] = m0;
+    if (mixes && i1 < M) mixes[t * M + i1] = m1;
+}
+
+__global__ __launch_bounds__(kGBlock) void mixes_finalize_kernel(const float* __restrict__ part, int nsplit,
+                                                                 int pg, int64_t n, int hc, int64_t d,
+                                                                 float norm_eps, float* __restrict__ mixes) {
+    const int64_t t = (int64_t)blockIdx.x * (kGBlock / 64) + (threadIdx.x >> 6);
+    if (t >= n) return;   // a whole wave leaves together
+    float m0, m1;
+    finalize_mixes_wave(part, nsplit, pg, n, hc, d, norm_eps, mixes, t, m0, m1);
+}
+
+// The finalize and the split in one launch: the split takes the token's mixes
+// from the finalizing wave's registers (the same fp32 values the two-kernel path
+// stores and reloads). kH = 2 or 8: butterfly sums; 0: any stream count.
+template <int kH>
+__global__ __launch_bounds__(kGBlock) void finalize_split_kernel(const float* __restrict__ part, int nsplit, int pg,
+                                                                 int64_t n, int hc, int64_t d, float norm_eps,
+                                                                 float* __restrict__ mixes,
+                                                                 const float* __restrict__ scale,
+                                                                 const float* __restrict__ base, int iters, float eps,
+                                                                 float* __restrict__ pre, float* __restrict__ post,
+                                                                 float* __restrict__ comb) {
+    const int64_t t = (int64_t)blockIdx.x * (kGBlock / 64) + (threadIdx.x >> 6);
+    if (t >= n) return;   // a whole wave leaves together
+    float m0, m1;
+    finalize_mixes_wave(part, nsplit, pg, n, hc, d, norm_eps, mixes, t, m0, m1);
+    auto mix = [&](int i) {   // every lane calls it: both shuffles run in all lanes
+        const float lo = __shfl(m0, i & 63), hi = __shfl(m1, i & 63);
+        return i < 64 ? lo : hi;
+    };
+    if constexpr (kH == 0)
+        split_generic_wave(mix, scale, base, t, hc, iters, eps, pre, post, comb);
+    else
+        split_butterfly_wave<kH>(mix, scale, base, t, iters, eps, pre, post, comb);
 }
 
 int64_t ceil_div_g(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -809,9 +864,21 @@ void launch_partial_bf16_t(const GenericPlan& p, const uint16_t* x, const float*
 
 // The projection's partial rows (with the collapse when y is given), then the
 // finalize into `mixes`.
+struct SplitArgs {   // the split fused into the finalize launch
+    const float* scale;
+    const float* base;
+    int iters;
+    float eps;
+    float* pre;
+    float* post;
+    float* comb;
+};
+
+// Projection partials, then the finalize (and, when `sp` is given, the split in the
+// same launch; `mixes` may then be null).
 hipError_t launch_projection(const void* x, bool bf16, int64_t n, int hc, int64_t d, const float* hc_fn,
                              float norm_eps, float* mixes, void* workspace, const float* pre_mix, void* y,
-                             hipStream_t stream) {
+                             hipStream_t stream, const SplitArgs* sp = nullptr) {
     const GenericPlan p = plan_generic(n, hc, d, bf16, y != nullptr);
     float* part = static_cast<float*>(workspace);
     if (bf16) {
@@ -824,8 +891,19 @@ hipError_t launch_projection(const void* x, bool bf16, int64_t n, int hc, int64_
         launch_partial_f32(p, x, hc_fn, n, hc, d, part, stream);
     }
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    hipLaunchKernelGGL(mixes_finalize_kernel, dim3((unsigned)ceil_div_g(n, kGBlock / 64)), dim3(kGBlock), 0, stream,
-                       part, p.nsplit, p.pg, n, hc, d, norm_eps, mixes);
+    const dim3 grid((unsigned)ceil_div_g(n, kGBlock / 64));
+    if (!sp)
+        hipLaunchKernelGGL(mixes_finalize_kernel, grid, dim3(kGBlock), 0, stream, part, p.nsplit, p.pg, n, hc, d,
+                           norm_eps, mixes);
+    else if (hc == 8)
+        hipLaunchKernelGGL(finalize_split_kernel<8>, grid, dim3(kGBlock), 0, stream, part, p.nsplit, p.pg, n, hc, d,
+                           norm_eps, mixes, sp->scale, sp->base, sp->iters, sp->eps, sp->pre, sp->post, sp->comb);
+    else if (hc == 2)
+        hipLaunchKernelGGL(finalize_split_kernel<2>, grid, dim3(kGBlock), 0, stream, part, p.nsplit, p.pg, n, hc, d,
+                           norm_eps, mixes, sp->scale, sp->base, sp->iters, sp->eps, sp->pre, sp->post, sp->comb);
+    else
+        hipLaunchKernelGGL(finalize_split_kernel<0>, grid, dim3(kGBlock), 0, stream, part, p.nsplit, p.pg, n, hc, d,
+                           norm_eps, mixes, sp->scale, sp->base, sp->iters, sp->eps, sp->pre, sp->post, sp->comb);
     return hipGetLastError();
 }
 
@@ -884,10 +962,9 @@ hipError_t launch_mixes_generic(const void* x, bool bf16, int64_t n, int hc, int
 }
 
 // expand (if any) -> projection (with the collapse fused for bf16 streams) ->
-// finalize -> split -> collapse (fp32 streams)
+// finalize + split (one launch) -> collapse (fp32 streams)
 hipError_t launch_fused_generic(const GenericRequest& r, hipStream_t stream) {
     const bool fused_pre = r.bf16 && r.y;
-    const GenericPlan p = plan_generic(r.n, r.hc, r.d, r.bf16, fused_pre);
     const void* src = r.res;
     if (r.f_prev) {
         if (hipError_t e = launch_post_generic(r.f_prev, r.res, r.bf16, r.post_prev, r.comb_prev, r.n, r.hc, r.d,
@@ -896,14 +973,10 @@ hipError_t launch_fused_generic(const GenericRequest& r, hipStream_t stream) {
             return e;
         src = r.streams_out;
     }
-    float* mixes = r.mixes ? r.mixes
-                           : reinterpret_cast<float*>(static_cast<char*>(r.workspace) + p.mixes_offset);
-    if (hipError_t e = launch_projection(src, r.bf16, r.n, r.hc, r.d, r.hc_fn, r.norm_eps, mixes, r.workspace,
-                                         fused_pre ? r.pre_mix : nullptr, fused_pre ? r.y : nullptr, stream);
-        e != hipSuccess)
-        return e;
-    if (hipError_t e = launch_split_generic(mixes, r.scale, r.base, r.n, r.hc, r.iters, r.eps, r.pre, r.post,
-                                            r.comb, stream);
+    // the finalize splits the mixes in the same launch; they are stored only when asked for
+    const SplitArgs sp{r.scale, r.base, r.iters, r.eps, r.pre, r.post, r.comb};
+    if (hipError_t e = launch_projection(src, r.bf16, r.n, r.hc, r.d, r.hc_fn, r.norm_eps, r.mixes, r.workspace,
+                                         fused_pre ? r.pre_mix : nullptr, fused_pre ? r.y : nullptr, stream, &sp);
         e != hipSuccess)
         return e;
     if (r.y && !fused_pre) return launch_pre_generic(src, r.bf16, r.pre_mix, r.n, r.hc, r.d, r.y, stream);
