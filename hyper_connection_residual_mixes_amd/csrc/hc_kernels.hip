@@ -153,8 +153,13 @@ struct Vec8 {
 __device__ __forceinline__ float sigmoid(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
 // One token's split. m: its 24 mixes. scale/base: the sublayer's parameters
-// (wave-uniform addresses: scalar loads). Normalisations multiply by a
-// reciprocal of (sum + eps) computed once per row or column.
+// (wave-uniform addresses: scalar loads). The Sinkhorn normalisations run in
+// factored form: after the first round's row softmax + eps gives K, every later
+// matrix is diag(r) K diag(c), and dividing row j by its sum + eps is the update
+// r_j <- r_j / (r_j (K c)_j + eps) (columns likewise with K^T r). That is 56 VALU
+// operations per round instead of 72 for rescaling all 16 entries; C = r_j K_jk c_k
+// is formed once at the end. Each division multiplies by a reciprocal of
+// (sum + eps) computed once per row or column.
 __device__ __forceinline__ void split_sinkhorn(const float (&m)[kMix], const float* __restrict__ scale,
                                                const float* __restrict__ base, int iters, float eps,
                                                float (&pre)[kHC], float (&post)[kHC],
@@ -165,37 +170,42 @@ __device__ __forceinline__ void split_sinkhorn(const float (&m)[kMix], const flo
         pre[j] = sigmoid(m[j] * s0 + base[j]) + eps;
         post[j] = 2.0f * sigmoid(m[kHC + j] * s1 + base[kHC + j]);
     }
+    float K[kHC * kHC];
 #pragma unroll
-    for (int i = 0; i < kHC * kHC; ++i) C[i] = m[2 * kHC + i] * s2 + base[2 * kHC + i];
-    // first round: row softmax (max subtracted), + eps, column normalisation
+    for (int i = 0; i < kHC * kHC; ++i) K[i] = m[2 * kHC + i] * s2 + base[2 * kHC + i];
+    // first round: row softmax (max subtracted), + eps
 #pragma unroll
     for (int j = 0; j < kHC; ++j) {
-        float mx = fmaxf(fmaxf(C[4 * j], C[4 * j + 1]), fmaxf(C[4 * j + 2], C[4 * j + 3]));
+        float mx = fmaxf(fmaxf(K[4 * j], K[4 * j + 1]), fmaxf(K[4 * j + 2], K[4 * j + 3]));
         float s = 0.f;
 #pragma unroll
         for (int k = 0; k < kHC; ++k) {
-            C[4 * j + k] = __expf(C[4 * j + k] - mx);
-            s += C[4 * j + k];
+            K[4 * j + k] = __expf(K[4 * j + k] - mx);
+            s += K[4 * j + k];
         }
         const float inv = __builtin_amdgcn_rcpf(s);
 #pragma unroll
-        for (int k = 0; k < kHC; ++k) C[4 * j + k] = C[4 * j + k] * inv + eps;
+        for (int k = 0; k < kHC; ++k) K[4 * j + k] = K[4 * j + k] * inv + eps;
     }
+    float r[kHC], c[kHC];
+#pragma unroll
+    for (int j = 0; j < kHC; ++j) r[j] = c[j] = 1.0f;
     auto cols = [&]() {
 #pragma unroll
         for (int k = 0; k < kHC; ++k) {
-            const float inv = __builtin_amdgcn_rcpf(C[k] + C[4 + k] + C[8 + k] + C[12 + k] + eps);
+            float v = K[k] * r[0];
 #pragma unroll
-            for (int j = 0; j < kHC; ++j) C[4 * j + k] *= inv;
+            for (int j = 1; j < kHC; ++j) v = fmaf(K[4 * j + k], r[j], v);
+            c[k] *= __builtin_amdgcn_rcpf(fmaf(c[k], v, eps));
         }
     };
     auto rows = [&]() {
 #pragma unroll
         for (int j = 0; j < kHC; ++j) {
-            const float inv =
-                __builtin_amdgcn_rcpf(C[4 * j] + C[4 * j + 1] + C[4 * j + 2] + C[4 * j + 3] + eps);
+            float u = K[4 * j] * c[0];
 #pragma unroll
-            for (int k = 0; k < kHC; ++k) C[4 * j + k] *= inv;
+            for (int k = 1; k < kHC; ++k) u = fmaf(K[4 * j + k], c[k], u);
+            r[j] *= __builtin_amdgcn_rcpf(fmaf(r[j], u, eps));
         }
     };
     cols();
@@ -203,6 +213,10 @@ __device__ __forceinline__ void split_sinkhorn(const float (&m)[kMix], const flo
         rows();
         cols();
     }
+#pragma unroll
+    for (int j = 0; j < kHC; ++j)
+#pragma unroll
+        for (int k = 0; k < kHC; ++k) C[4 * j + k] = r[j] * K[4 * j + k] * c[k];
 }
 
 __device__ __forceinline__ void store_coeffs(int64_t t, const float (&pre)[kHC], const float (&post)[kHC],
