@@ -45,6 +45,22 @@ def test_split(hc_, n, iters):
         check(f"hc={hc_} n={n} it={iters} {name}", gg, r, TOL_F32, rho=1.0)
 
 
+@pytest.mark.parametrize("hc_", HCS)
+def test_split_large_eps(hc_):
+    """eps = 0.3, so that where it enters each normalisation shows far above the
+    tolerance."""
+    g = hc_inputs.generator(60 + hc_)
+    M = (2 + hc_) * hc_
+    m = hc_inputs.normal(g, (300, M), 2.0)
+    s = torch.rand(3, generator=g) * 1.5 + 0.5
+    b = hc_inputs.normal(g, (M,), 0.1)
+    ref = oracle.hc_split_sinkhorn(m, s, b, hc_mult=hc_, sinkhorn_iters=5, eps=0.3)
+    got = hc.hc_split_sinkhorn(*to_dev((m, s, b)), hc_mult=hc_, sinkhorn_iters=5, eps=0.3)
+    sync()
+    for name, gg, r in zip(("pre", "post", "comb"), got, ref):
+        check(f"hc={hc_} eps=0.3 {name}", gg, r, TOL_F32, rho=1.0)
+
+
 # ------------------------------------------------------------- pre / post
 CASES = [(torch.float32, 37, 264), (torch.bfloat16, 37, 264), (torch.bfloat16, 1, 8),
          (torch.bfloat16, 64, 5120)]

@@ -59,6 +59,32 @@ def test_split_ragged_rows_and_rounds(n, iters):
         check(f"n={n} it={iters} {name}", gg, r, TOL_F32, rho=1.0)
 
 
+@pytest.mark.parametrize("eps", [0.05, 0.5])
+@pytest.mark.parametrize("iters", [2, 7])
+def test_split_large_eps(eps, iters):
+    """An eps large enough that where it enters each normalisation shows far above the
+    tolerance (at the default 1e-6 a misplaced eps would move results by ~1e-6 only):
+    the standalone split (one lane per row, factored rounds) and the fused boundary's
+    split (16 lanes per token), both against the oracle."""
+    g = hc_inputs.generator(8)
+    m = hc_inputs.normal(g, (300, 24), 2.0)
+    s = torch.rand(3, generator=g) * 1.5 + 0.5
+    b = hc_inputs.normal(g, (24,), 0.1)
+    ref = oracle.hc_split_sinkhorn(m, s, b, sinkhorn_iters=iters, eps=eps)
+    got = hc.hc_split_sinkhorn(*to_dev((m, s, b)), sinkhorn_iters=iters, eps=eps)
+    sync()
+    for name, gg, r in zip(("pre", "post", "comb"), got, ref):
+        check(f"eps={eps} it={iters} {name}", gg, r, TOL_F32, rho=1.0)
+    inp = hc_inputs.tiny(seed=3)
+    pi = oracle_pi(inp)
+    ref = oracle.fused_step(inp["x"], *inp["attn"], pre_mix=pi, sinkhorn_iters=iters, eps=eps)
+    got = hc.hc_fused_step(*to_dev((inp["x"],)), *to_dev(inp["attn"]), pre_mix=to_dev(pi),
+                           sinkhorn_iters=iters, eps=eps)
+    sync()
+    for k in ("pre", "post", "comb"):
+        check(f"fused eps={eps} it={iters} {k}", got[k], ref[k], TOL_F32, rho=1.0)
+
+
 # ------------------------------------------------------------- pre / post
 CASES = [(torch.float32, 16, 256), (torch.float32, 37, 264), (torch.bfloat16, 37, 264),
          (torch.bfloat16, 1, 8), (torch.bfloat16, 64, 5120)]
