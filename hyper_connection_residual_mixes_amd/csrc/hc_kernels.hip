@@ -1227,9 +1227,14 @@ __global__ __launch_bounds__(kSwBlock) void bf16_sweep2_kernel(PassArgs a) {
     for (int T = 0; T < 8; ++T) acc[T][0] = acc[T][1] = floatx4_t{0.f, 0.f, 0.f, 0.f};
     float ssq[2] = {0.f, 0.f};
 
-    auto step = [&](int s, StepRegs2<kPost>& cur, StepRegs2<kPost>& ahead, float4 (&Wcur)[4], float4 (&Wnext)[4]) {
+    // Stream prefetch: with the expand, the set just consumed takes step s + 2 right
+    // after the rowwise work of step s, before the barrier and the MFMAs; without
+    // it, step s + 1 is issued into the other set at the start of step s (measured:
+    // each order is the faster one for its instance).
+    auto step = [&](int s, StepRegs2<kPost>& cur, StepRegs2<kPost>& ahead, float4 (&Wcur)[4],
+                    float4 (&Wnext)[4]) {
         load_b(Wnext, s + 1);
-        load_step(ahead, s + 1);
+        if constexpr (!kPost) load_step(ahead, s + 1);
         const int64_t cs = c_begin + (int64_t)s * kStep;
         const bool ok = cs + c8 * 8 < c_end;
         const uint32_t so = (uint32_t)(cs * 2);
@@ -1298,6 +1303,7 @@ __global__ __launch_bounds__(kSwBlock) void bf16_sweep2_kernel(PassArgs a) {
 #pragma unroll
             for (int j = 0; j < kHC; ++j) A[a_slot(tl, j, c8)] = cur.x[h][j];
         }
+        if constexpr (kPost) load_step(cur, s + 2);
         __syncthreads();
         uint4 Bcur[kFragsPerKb], hi1, mid1, lo1;
         split3(Wcur[0], Wcur[1], Bcur[0], Bcur[1], Bcur[2]);
@@ -1321,6 +1327,7 @@ __global__ __launch_bounds__(kSwBlock) void bf16_sweep2_kernel(PassArgs a) {
     float4 B0[4], B1[4];
     load_b(B0, 0);
     load_step(R0, 0);
+    if constexpr (kPost) load_step(R1, 1);
     __syncthreads();   // the coefficients are in LDS
     int s = 0;
     for (; s + 2 <= nst; s += 2) {
