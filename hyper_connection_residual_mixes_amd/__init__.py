@@ -18,7 +18,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libhc.so")
+# HC_LIBRARY names another build of the same library (the host-sanitizer test uses it)
+LIB_PATH = os.environ.get("HC_LIBRARY") or os.path.join(_PKG, "libhc.so")
 
 HC_F32, HC_BF16 = 0, 1
 HC_MULT, SINKHORN_ITERS, HC_EPS, NORM_EPS = 4, 20, 1e-6, 1e-20

@@ -36,5 +36,24 @@ def build(out: str = LIB_PATH, extra_flags=(), sources=None) -> str:
     return out
 
 
+def build_host_sanitized(out: str) -> str:
+    """The same library with AddressSanitizer and UndefinedBehaviorSanitizer on its
+    host code only (the device code is built as usual); every finding aborts. For
+    CPU tests of the C-ABI validation: load it with the clang ASan runtime
+    preloaded (``sanitizer_runtime()``)."""
+    flags = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=all", "-shared-libsan", "-fno-omit-frame-pointer"]
+    return build(out=out, extra_flags=flags)
+
+
+def sanitizer_runtime() -> str:
+    """Path of the clang ASan runtime that a host-sanitized build needs preloaded."""
+    r = subprocess.run([hipcc(), "--print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("clang ASan runtime not found")
+    return path
+
+
 if __name__ == "__main__":
     print(build())

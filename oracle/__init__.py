@@ -47,7 +47,9 @@ def build(sanitize: bool = False, src: str = _SRC, out: str | None = None,
     if werror:
         cmd.insert(-5, "-Werror")
     if sanitize:
-        cmd[1:1] = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-g"]
+        # every finding is fatal (no recovery), so a sanitized run fails loudly
+        cmd[1:1] = ["-fsanitize=address,undefined", "-fsanitize=float-cast-overflow",
+                    "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
     subprocess.run(cmd, check=True)
     os.replace(out + ".tmp", out)
     return out

@@ -81,9 +81,10 @@ static uint16_t double_to_bf16_bits(double v)
         double s = nearbyint(ldexp(m, 8));  /* 8 significant bits, ties-to-even */
         q = ldexp(s, e - 8);
     }
-    float qf = (float)q;                    /* exact: q has <= 8 significant bits */
-    if (q >= ldexp(1.0, 128))
-        qf = INFINITY;
+    /* exact below 2^128 (q has <= 8 significant bits); 2^128 and beyond is
+     * infinity, tested before the conversion (a double out of the float range
+     * has no defined conversion) */
+    float qf = q >= ldexp(1.0, 128) ? INFINITY : (float)q;
     if (v < 0)
         qf = -qf;
     uint32_t u;

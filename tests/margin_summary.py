@@ -1,0 +1,55 @@
+"""Summarise a parity-margin log into markdown.
+
+The GPU tests append one line per comparison to the file named by HC_PARITY_LOG
+(test id, check name, worst relative error, tolerance; see tests/parity.py). This
+script reads such a log and prints, per tolerance, the checks closest to their
+bound, and the worst teacher-forced error per output kind.
+
+    python tests/margin_summary.py gpurun_out/margins.tsv > tests/parity_margins.md
+"""
+import sys
+from collections import defaultdict
+
+
+def main(path: str, command: str) -> None:
+    rows = []
+    for line in open(path):
+        test, name, err, tol = line.rstrip("\n").split("\t")
+        rows.append((test.split("::", 1)[-1], test.split("::", 1)[0], name, float(err), float(tol)))
+    print("# Parity margins of the GPU tests")
+    print()
+    print("Worst relative error of every comparison in one run of the GPU parity tests,")
+    print("`|got - ref| / max(|ref|, rho)` (rho as in tests/parity.py), against its tolerance.")
+    print()
+    print(f"Command: `{command}`")
+    print()
+    print(f"{len(rows)} comparisons, {len({r[0] for r in rows})} test cases, "
+          f"worst ratio to tolerance {max(r[3] / r[4] for r in rows):.3f}.")
+    print()
+    print("## Teacher-forced checks (the oracle fed the GPU's own inputs of the step)")
+    print()
+    print("| output | worst rel. error | tolerance | ratio | where |")
+    print("|---|---|---|---|---|")
+    kinds = defaultdict(list)
+    for r in rows:
+        if "GPU x1" in r[2] or "teacher-forced" in r[2] or "same inputs" in r[2]:
+            key = r[2].split("(")[0].split()[-1] if "teacher-forced" not in r[2] else r[2].split(",")[0].split()[-1]
+            kinds[(key, r[4])].append(r)
+    for (key, tol), rs in sorted(kinds.items(), key=lambda kv: (kv[0][1], kv[0][0])):
+        w = max(rs, key=lambda r: r[3])
+        print(f"| {key} | {w[3]:.3e} | {tol:g} | {w[3] / tol:.3f} | `{w[0]}` ({len(rs)} checks) |")
+    for tol in sorted({r[4] for r in rows}):
+        sel = sorted((r for r in rows if r[4] == tol), key=lambda r: -r[3])
+        print()
+        print(f"## Tolerance {tol:g}: the 15 closest of {len(sel)} checks")
+        print()
+        print("| rel. error | ratio | test | check |")
+        print("|---|---|---|---|")
+        for r in sel[:15]:
+            print(f"| {r[3]:.3e} | {r[3] / tol:.3f} | `{r[0]}` | {r[2]} |")
+
+
+if __name__ == "__main__":
+    main(sys.argv[1], sys.argv[2] if len(sys.argv) > 2 else
+         "HC_PARITY_LOG=gpurun_out/margins.tsv python -u -m pytest tests -m gpu -x -q --timeout 300 "
+         "--timeout-method thread")

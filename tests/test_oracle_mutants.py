@@ -40,6 +40,10 @@ MUTANTS = {
                                            "(double)comb[(t * hc + k) * hc + j]"),
     "post drops f": ("(double)post[t * hc + k] * load_elem(f, dtype, t * d + e)", "0.0"),
     "bf16 truncation instead of rounding": ("nearbyint(ldexp(m, 8))", "floor(ldexp(m, 8))"),
+    "bf16 subnormal grid 2^-134": ("nearbyint(ldexp(a, 133)), -133)", "nearbyint(ldexp(a, 134)), -134)"),
+    "bf16 subnormal truncated": ("ldexp(nearbyint(ldexp(a, 133)), -133)", "ldexp(floor(ldexp(a, 133)), -133)"),
+    "bf16 overflow saturates": ("q >= ldexp(1.0, 128) ? INFINITY : (float)q",
+                                "q >= ldexp(1.0, 128) ? 0x1.fep127f : (float)q"),
     "rmsnorm mean over d - 1": ("sqrt(ss / (double)d + eps)", "sqrt(ss / (double)(d - 1) + eps)"),
     "rmsnorm gain dropped": ("* r * (double)gain[e]", "* r"),
     "rmsnorm eps replaced": ("sqrt(ss / (double)d + eps)", "sqrt(ss / (double)d + 1e-6)"),

@@ -53,6 +53,38 @@ def test_bf16_rounding_ties_to_even():
     assert oracle.round_bf16_bits(0.0) == 0
 
 
+def test_bf16_rounding_subnormal_range():
+    """Below 2^-126 bf16 keeps the fp32 subnormal grid, multiples of 2^-133 (Diagram
+    block "Cast": nearest representable number; ties to even). Hand-worked values:
+    the grid point itself, ties on both sides of an even unit, the tie at half a unit
+    (to zero), and the largest subnormal rounding up into the smallest normal."""
+    u = 2.0**-133
+    assert oracle.round_bf16_bits(u) == 0x0001
+    assert oracle.round_bf16_bits(1.5 * u) == 0x0002      # tie 1 | 2 -> 2 (even)
+    assert oracle.round_bf16_bits(2.5 * u) == 0x0002      # tie 2 | 3 -> 2 (even)
+    assert oracle.round_bf16_bits(0.5 * u) == 0x0000      # tie 0 | 1 -> 0 (even)
+    assert oracle.round_bf16_bits(0.5000001 * u) == 0x0001
+    assert oracle.round_bf16_bits(-3.0 * u) == 0x8003
+    assert oracle.round_bf16_bits(126.5 * u) == 0x007E    # tie 126 | 127 -> 126
+    assert oracle.round_bf16_bits(127.5 * u) == 0x0080    # tie 127 | 128 -> 2^-126 (normal)
+    assert oracle.round_bf16_bits(2.0**-126 - 2.0**-136) == 0x0080
+    assert oracle.round_bf16_bits(1e-45) == 0x0000        # far below half a unit
+
+
+def test_bf16_rounding_overflow_range():
+    """Top of the range: the largest finite bf16 is (2 - 2^-7) * 2^127 (0x7F7F); the
+    midpoint to 2^128 rounds to the even neighbour, which is infinity; beyond it
+    everything is infinity with the sign kept."""
+    top = (2.0 - 2.0**-7) * 2.0**127
+    assert oracle.round_bf16_bits(top) == 0x7F7F
+    assert oracle.round_bf16_bits((2.0 - 2.0**-8 - 2.0**-20) * 2.0**127) == 0x7F7F
+    assert oracle.round_bf16_bits((2.0 - 2.0**-8) * 2.0**127) == 0x7F80   # tie -> even (inf)
+    assert oracle.round_bf16_bits(2.0**128) == 0x7F80
+    assert oracle.round_bf16_bits(1e39) == 0x7F80
+    assert oracle.round_bf16_bits(-1e300) == 0xFF80
+    assert oracle.round_bf16_bits(-top) == 0xFF7F
+
+
 def test_bf16_rounding_matches_torch_on_fp32_values():
     """Library routine: torch's fp32 -> bf16 conversion is round-to-nearest-even; on
     fp32-representable inputs the oracle's direct fp64 -> bf16 rounding must agree."""
