@@ -56,7 +56,10 @@ def lib():
     L.hc_rmsnorm_mxfp8.argtypes = [P, I, P, I64, I64, F, P, P, P, P]
     L.hc_fused_step.argtypes = [P, P, P, P, P, P, P, P, I64, I, I64, I, F, I, F,
                                 P, P, P, P, P, P, P, SZ, P]
-    for name in ("hc_mixes", "hc_split_sinkhorn", "hc_pre", "hc_post", "hc_fused_step", "hc_rmsnorm_mxfp8"):
+    L.hc_fused_step_noalloc.argtypes = [P, P, P, P, P, P, P, P, I64, I, I64, I, F, I, F,
+                                        P, P, P, P, P, P, P]
+    for name in ("hc_mixes", "hc_split_sinkhorn", "hc_pre", "hc_post", "hc_fused_step", "hc_fused_step_noalloc",
+                 "hc_rmsnorm_mxfp8"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -255,7 +258,26 @@ def hc_fused_step(residual, hc_fn, hc_scale, hc_base, pre_mix=None, f_prev=None,
     this sublayer's coefficients and the collapse with ``pre_mix``.
 
     Returns dict(streams, y, pre, post, comb, mixes) (streams is ``residual`` when
-    ``f_prev`` is None; y / mixes are None when not requested)."""
+    ``f_prev`` is None; y / mixes are None when not requested; ``want_mixes`` may
+    also be the output tensor itself)."""
+    return _fused_step(residual, hc_fn, hc_scale, hc_base, pre_mix, f_prev, post_prev, comb_prev,
+                       sinkhorn_iters, eps, norm_eps, streams_out, y, out, want_mixes, want_y, workspace,
+                       noalloc=False)
+
+
+def hc_fused_step_noalloc(residual, hc_fn, hc_scale, hc_base, pre_mix=None, f_prev=None, post_prev=None,
+                          comb_prev=None, sinkhorn_iters=SINKHORN_ITERS, eps=HC_EPS, norm_eps=NORM_EPS,
+                          streams_out=None, y=None, out=None, want_mixes=False, want_y=True):
+    """``hc_fused_step`` on the library's static device scratch instead of a
+    workspace (C entry point ``hc_fused_step_noalloc``). The library allocates
+    nothing; with every output tensor passed in, neither does this call."""
+    return _fused_step(residual, hc_fn, hc_scale, hc_base, pre_mix, f_prev, post_prev, comb_prev,
+                       sinkhorn_iters, eps, norm_eps, streams_out, y, out, want_mixes, want_y, None,
+                       noalloc=True)
+
+
+def _fused_step(residual, hc_fn, hc_scale, hc_base, pre_mix, f_prev, post_prev, comb_prev, sinkhorn_iters,
+                eps, norm_eps, streams_out, y, out, want_mixes, want_y, workspace, noalloc):
     _dev(residual, "residual")
     lead, n, hc, d = _streams_shape(residual)
     dev = residual.device
@@ -286,15 +308,23 @@ def hc_fused_step(residual, hc_fn, hc_scale, hc_base, pre_mix=None, f_prev=None,
     _size(_dev(pre, "pre", torch.float32), n * hc, "pre", dev)
     _size(_dev(post, "post", torch.float32), n * hc, "post", dev)
     _size(_dev(comb, "comb", torch.float32), n * hc * hc, "comb", dev)
-    mixes = torch.empty(*lead, (2 + hc) * hc, dtype=torch.float32, device=dev) if want_mixes else None
-    ws, ws_bytes = _workspace(n, hc, d, dev, workspace)
-    _check("hc_fused_step", lib().hc_fused_step(
-        _ptr(residual), _ptr(f_prev), _ptr(post_prev) if expand else None,
-        _ptr(comb_prev) if expand else None, _ptr(pre_mix) if want_y else None,
-        _ptr(_dev(hc_fn, "hc_fn", torch.float32)), _ptr(_dev(hc_scale, "hc_scale", torch.float32)),
-        _ptr(_dev(hc_base, "hc_base", torch.float32)), n, hc, d, _dtype_code(residual),
-        float(norm_eps), int(sinkhorn_iters), float(eps), _ptr(streams_out) if expand else None,
-        _ptr(y), _ptr(pre), _ptr(post), _ptr(comb), _ptr(mixes), _ptr(ws), ws_bytes, _stream(dev)))
+    if isinstance(want_mixes, torch.Tensor):   # the caller's mixes tensor
+        mixes = _size(_dev(want_mixes, "mixes", torch.float32), n * (2 + hc) * hc, "mixes", dev)
+    elif want_mixes:
+        mixes = torch.empty(*lead, (2 + hc) * hc, dtype=torch.float32, device=dev)
+    else:
+        mixes = None
+    args = (_ptr(residual), _ptr(f_prev), _ptr(post_prev) if expand else None,
+            _ptr(comb_prev) if expand else None, _ptr(pre_mix) if want_y else None,
+            _ptr(_dev(hc_fn, "hc_fn", torch.float32)), _ptr(_dev(hc_scale, "hc_scale", torch.float32)),
+            _ptr(_dev(hc_base, "hc_base", torch.float32)), n, hc, d, _dtype_code(residual),
+            float(norm_eps), int(sinkhorn_iters), float(eps), _ptr(streams_out) if expand else None,
+            _ptr(y), _ptr(pre), _ptr(post), _ptr(comb), _ptr(mixes))
+    if noalloc:
+        _check("hc_fused_step_noalloc", lib().hc_fused_step_noalloc(*args, _stream(dev)))
+    else:
+        ws, ws_bytes = _workspace(n, hc, d, dev, workspace)
+        _check("hc_fused_step", lib().hc_fused_step(*args, _ptr(ws), ws_bytes, _stream(dev)))
     return dict(streams=streams_out if expand else residual, y=y, pre=pre, post=post, comb=comb,
                 mixes=mixes)
 

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_PATH = os.path.join(PKG, "libhc.so")
 SOURCES = [os.path.join(CSRC, "hc_kernels.hip"), os.path.join(CSRC, "hc_generic.hip"),
-           os.path.join(CSRC, "hc_abi.cpp")]
+           os.path.join(CSRC, "hc_noalloc.hip"), os.path.join(CSRC, "hc_abi.cpp")]
 
 # Packed-FP32 VALU forms are switched off for all device code.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

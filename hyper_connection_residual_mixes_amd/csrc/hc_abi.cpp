@@ -92,6 +92,8 @@ const char* hc_status_string(int status) {
         case HC_ERR_ALIAS: return "an output overlaps an input or another output";
         case HC_ERR_WORKSPACE: return "workspace missing or too small";
         case HC_ERR_HIP: return "the HIP runtime reported an error";
+        case HC_ERR_SCRATCH:
+            return "the call needs more scratch than the no-allocation entry point's static buffer holds";
         default: return "unknown status";
     }
 }
@@ -216,11 +218,18 @@ int hc_mixes(const void* x, int dtype, int64_t n, int hc, int64_t d, const float
     return hip_status(hc::launch_pass_and_finalize(r, static_cast<hipStream_t>(stream)));
 }
 
-int hc_fused_step(const void* residual, const void* f_prev, const float* post_prev, const float* comb_prev,
-                  const float* pre_mix, const float* hc_fn, const float* hc_scale, const float* hc_base,
-                  int64_t n, int hc, int64_t d, int dtype, float norm_eps, int sinkhorn_iters, float eps,
-                  void* streams_out, void* y, float* pre, float* post, float* comb, float* mixes,
-                  void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// hc_fused_step and hc_fused_step_noalloc. With noalloc the workspace arguments
+// are ignored: the scratch is the library's static device array, looked up (the
+// first HIP call) only after every argument has been validated.
+int fused_step(const void* residual, const void* f_prev, const float* post_prev, const float* comb_prev,
+               const float* pre_mix, const float* hc_fn, const float* hc_scale, const float* hc_base, int64_t n,
+               int hc, int64_t d, int dtype, float norm_eps, int sinkhorn_iters, float eps, void* streams_out,
+               void* y, float* pre, float* post, float* comb, float* mixes, void* workspace,
+               size_t workspace_bytes, void* stream, bool noalloc) {
     if (int rc = check_shape(n, hc, d, dtype)) return rc;
     if (check_eps(norm_eps) != HC_OK || check_eps(eps) != HC_OK || sinkhorn_iters < 1) return HC_ERR_ARG;
     if (n == 0) return HC_OK;
@@ -229,10 +238,16 @@ int hc_fused_step(const void* residual, const void* f_prev, const float* post_pr
     if (expand && (!post_prev || !comb_prev || !streams_out)) return HC_ERR_NULL;
     if (y && !pre_mix) return HC_ERR_NULL;
     const size_t ws_need = ws_bytes(n, hc, d);
-    if (!workspace || workspace_bytes < ws_need) return HC_ERR_WORKSPACE;
+    if (noalloc) {
+        if (ws_need > (size_t)HC_NOALLOC_SCRATCH_BYTES) return HC_ERR_SCRATCH;
+        workspace = nullptr;   // the static scratch: no caller memory to check
+        workspace_bytes = 0;
+    } else if (!workspace || workspace_bytes < ws_need) {
+        return HC_ERR_WORKSPACE;
+    }
     const void* a16[] = {residual, hc_fn, pre, post, comb, workspace};
     for (const void* p : a16)
-        if (!aligned(p, 16)) return HC_ERR_ALIGN;
+        if (p && !aligned(p, 16)) return HC_ERR_ALIGN;
     const void* o16[] = {f_prev, post_prev, comb_prev, pre_mix, streams_out, y, mixes};
     for (const void* p : o16)
         if (p && !aligned(p, 16)) return HC_ERR_ALIGN;
@@ -247,7 +262,7 @@ int hc_fused_step(const void* residual, const void* f_prev, const float* post_pr
                          {post, un * uh * 4},
                          {comb, un * uh * uh * 4},
                          {mixes, un * M * 4},
-                         {workspace, ws_need}};
+                         {workspace, workspace ? ws_need : 0}};
     const Span ins[] = {res_span,
                         {f_prev, un * ud * es},
                         {expand ? post_prev : nullptr, un * uh * 4},
@@ -258,6 +273,9 @@ int hc_fused_step(const void* residual, const void* f_prev, const float* post_pr
                         {hc_base, M * 4}};
     const Span allowed[] = {so_span, res_span};
     if (int rc = check_aliases(outs, 7, ins, 8, allowed, 1)) return rc;
+    if (noalloc) {
+        if (hc::noalloc_scratch(static_cast<hipStream_t>(stream), &workspace) != hipSuccess) return HC_ERR_HIP;
+    }
 
     if (hc != kHC) {
         hc::GenericRequest g{};
@@ -310,6 +328,30 @@ int hc_fused_step(const void* residual, const void* f_prev, const float* post_pr
     r.iters = sinkhorn_iters;
     r.eps = eps;
     return hip_status(hc::launch_pass_and_finalize(r, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int hc_fused_step(const void* residual, const void* f_prev, const float* post_prev, const float* comb_prev,
+                  const float* pre_mix, const float* hc_fn, const float* hc_scale, const float* hc_base,
+                  int64_t n, int hc, int64_t d, int dtype, float norm_eps, int sinkhorn_iters, float eps,
+                  void* streams_out, void* y, float* pre, float* post, float* comb, float* mixes,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+    return fused_step(residual, f_prev, post_prev, comb_prev, pre_mix, hc_fn, hc_scale, hc_base, n, hc, d, dtype,
+                      norm_eps, sinkhorn_iters, eps, streams_out, y, pre, post, comb, mixes, workspace,
+                      workspace_bytes, stream, false);
+}
+
+int hc_fused_step_noalloc(const void* residual, const void* f_prev, const float* post_prev,
+                          const float* comb_prev, const float* pre_mix, const float* hc_fn,
+                          const float* hc_scale, const float* hc_base, int64_t n, int hc, int64_t d,
+                          int dtype, float norm_eps, int sinkhorn_iters, float eps, void* streams_out,
+                          void* y, float* pre, float* post, float* comb, float* mixes, void* stream) {
+    return fused_step(residual, f_prev, post_prev, comb_prev, pre_mix, hc_fn, hc_scale, hc_base, n, hc, d, dtype,
+                      norm_eps, sinkhorn_iters, eps, streams_out, y, pre, post, comb, mixes, nullptr, 0, stream,
+                      true);
 }
 
 }  // extern "C"

@@ -95,6 +95,10 @@ struct GenericRequest {
 };
 
 size_t generic_workspace_bytes(int64_t n, int hc, int64_t d);
+
+// Device address of the static no-allocation scratch (HC_NOALLOC_SCRATCH_BYTES)
+// on the device of `stream`; looked up once per device (hc_noalloc.hip).
+hipError_t noalloc_scratch(hipStream_t stream, void** out);
 hipError_t launch_split_generic(const float* mixes, const float* scale, const float* base, int64_t n, int hc,
                                 int iters, float eps, float* pre, float* post, float* comb, hipStream_t stream);
 hipError_t launch_pre_generic(const void* x, bool bf16, const float* pre_mix, int64_t n, int hc, int64_t d, void* y,

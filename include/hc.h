@@ -74,6 +74,10 @@ extern "C" {
 #define HC_ERR_ALIAS (-6)       /* outputs overlap inputs or each other */
 #define HC_ERR_WORKSPACE (-7)   /* workspace missing or smaller than required */
 #define HC_ERR_HIP (-8)         /* the HIP runtime reported an error */
+#define HC_ERR_SCRATCH (-9)     /* hc_fused_step_noalloc: needs more than the static scratch */
+
+/* Bytes of the static device scratch behind hc_fused_step_noalloc (per GPU). */
+#define HC_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 #define HC_F32 0
 #define HC_BF16 1
@@ -185,6 +189,31 @@ int hc_fused_step(const void* residual, const void* f_prev, const float* post_pr
                   int dtype, float norm_eps, int sinkhorn_iters, float eps, void* streams_out,
                   void* y, float* pre, float* post, float* comb, float* mixes,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * hc_fused_step without a workspace argument, for callers that cannot allocate
+ * device memory: code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid hipMalloc. Same arguments, validation, kernels and
+ * results as hc_fused_step; its scratch (the per-slice partial rows) is a static
+ * device array of HC_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it
+ * runs on until the process ends, looked up on a device's first call. The call
+ * allocates nothing and never synchronises.
+ *   - Sizes whose hc_workspace_size(n, hc, d) exceeds HC_NOALLOC_SCRATCH_BYTES are
+ *     rejected with HC_ERR_SCRATCH before anything is enqueued (at d = 5120: up to
+ *     262,144 tokens with four streams, 2,438 with eight).
+ *   - All calls on one GPU share that GPU's scratch. Calls ordered on one stream
+ *     are safe; calls that may overlap on one GPU (other streams without an
+ *     ordering between them, other threads) race and must not be issued.
+ *   - Nothing in the scratch has to start at zero: every partial row is written
+ *     before it is read, so a previous call's contents do not matter.
+ *   - HC_ERR_HIP also reports a failed lookup of the scratch's device address.
+ */
+int hc_fused_step_noalloc(const void* residual, const void* f_prev, const float* post_prev,
+                          const float* comb_prev, const float* pre_mix, const float* hc_fn,
+                          const float* hc_scale, const float* hc_base, int64_t n, int hc,
+                          int64_t d, int dtype, float norm_eps, int sinkhorn_iters, float eps,
+                          void* streams_out, void* y, float* pre, float* post, float* comb,
+                          float* mixes, void* stream);
 
 #ifdef __cplusplus
 }

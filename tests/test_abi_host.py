@@ -36,7 +36,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for want in ("hc_mixes", "hc_split_sinkhorn", "hc_pre", "hc_post", "hc_fused_step",
+    for want in ("hc_mixes", "hc_split_sinkhorn", "hc_pre", "hc_post", "hc_fused_step", "hc_fused_step_noalloc",
                  "hc_rmsnorm_mxfp8", "hc_workspace_size", "hc_status_string", "hc_abi_version"):
         assert want in names
 
@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol():
 def test_version_and_status_strings():
     L = hc.lib()
     assert L.hc_abi_version() == 1
-    for s in range(-8, 1):
+    for s in range(-9, 1):
         assert hc.status_string(s) and hc.status_string(s) != "unknown status"
     assert hc.status_string(-99) == "unknown status"
 
@@ -252,3 +252,28 @@ def test_fused_generic_validation():
     assert fused(comb=0x70001000 + 16 * 5 * 4 - 16) == ALIAS    # comb overlaps post
     assert fused(f_prev=0x58000000, post_prev=0x59000000, comb_prev=0x59001000,
                  so=A + 16) == ALIAS                           # partial overlap with residual
+
+
+def _fused_noalloc(res=A, pre_mix=0x50000000, fn=B, scale=C, base=C + 64, hc_=4, n=16, d=256, dtype=1,
+                   iters=20, y=0x60000000, pre=0x70000000, post=0x70001000, comb=0x70002000, mixes=None):
+    return hc.lib().hc_fused_step_noalloc(P(res), None, None, None, P(pre_mix), P(fn), P(scale), P(base), n, hc_, d,
+                                          dtype, 1e-20, iters, 1e-6, None, P(y), P(pre), P(post), P(comb),
+                                          P(mixes), None)
+
+
+def test_fused_noalloc_validation():
+    """The no-allocation variant validates like hc_fused_step (no workspace
+    arguments) and refuses, before any HIP call, a size whose scratch need exceeds
+    the static buffer (HC_ERR_SCRATCH)."""
+    assert _fused_noalloc(n=0) == OK
+    assert _fused_noalloc(iters=0) == ARG
+    assert _fused_noalloc(pre=None) == NULL
+    assert _fused_noalloc(scale=C + 2) == ALIGN
+    assert _fused_noalloc(post=0x70000000 + 16 * 4 * 4 - 16) == ALIAS
+    assert _fused_noalloc(n=1 << 40, d=1 << 20) == SHAPE
+    assert hc.workspace_size(4096, 8, 5120) > 32 << 20
+    assert _fused_noalloc(hc_=8, n=4096, d=5120) == -9
+    assert _fused_noalloc(n=262145, d=5120) == -9            # four streams: 128 B per token beyond 2^18
+    # within the buffer, validation passes and the first HIP call (no GPU here) fails
+    assert _fused_noalloc(n=262144, d=5120, y=0x7000000000, pre=0x7100000000, post=0x7200000000,
+                          comb=0x7300000000, pre_mix=0x7400000000, res=0x1000000000) == HIP
