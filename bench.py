@@ -78,6 +78,58 @@ def stored_traffic(entry: str):
     return rec.get("bytes_per_launch", {}).get(entry)
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), or "unknown"."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def copy_ceiling(dev, nbytes: int = 1 << 30, reps: int = 10):
+    """The plain-copy reference (bench_copy.hip, a grid-stride copy of 16-byte
+    elements) on `nbytes` in + `nbytes` out, with cached and with non-temporal
+    stores at three grid sizes; HIP events on the launch stream, median of `reps`
+    after 3 warm-up copies. Returns (best GB/s, all figures)."""
+    import ctypes
+    import statistics
+    import torch
+    path = os.path.join(ROOT, "bench_copy.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing (run __graft_entry__.build())")
+    L = ctypes.CDLL(path)
+    L.bench_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                             ctypes.c_void_p]
+    L.bench_copy.restype = ctypes.c_int
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    stream = torch.cuda.current_stream(dev)
+    figures = {}
+    for nt in (0, 1):
+        for wgs in (1024, 2048, 4096):
+            def run():
+                rc = L.bench_copy(src.data_ptr(), dst.data_ptr(), nbytes, nt, wgs, stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"bench_copy failed ({rc})")
+            for _ in range(3):
+                run()
+            times = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                run()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1) * 1e-3)
+            figures[f"{'nontemporal' if nt else 'cached'}_{wgs}wg"] = 2 * nbytes / statistics.median(times) / 1e9
+    del src, dst
+    return max(figures.values()), figures
+
+
 def cpu_baseline(sets_cpu):
     """The C oracle (fp64, one thread) on the whole block for each input set."""
     import oracle
@@ -90,7 +142,7 @@ def cpu_baseline(sets_cpu):
         dt += time.perf_counter() - t0
         n_tok += x.shape[0]
     d = sets_cpu[0][0].shape[-1]
-    return dict(value=n_tok / dt, unit="tokens/s", cores=1, kind="oracle",
+    return dict(value=n_tok / dt, unit="tokens/s", cores=1, kind="oracle", cpu_model=cpu_model(),
                 sample=f"the full block (attention + FFN boundary) on {len(sets_cpu)} input sets of "
                        f"{sets_cpu[0][0].shape[0]} tokens, d={d}: {n_tok} tokens, "
                        f"single-threaded C oracle in fp64, {dt:.1f} s")
@@ -115,7 +167,7 @@ def cpu_baseline_threads(sets_cpu, max_threads: int = 16):
                                                  fa[cuts[i]:cuts[i + 1]], ff[cuts[i]:cuts[i + 1]]), range(cores)))
             dt += time.perf_counter() - t0
             n_tok += n
-    return dict(value=n_tok / dt, unit="tokens/s", cores=cores, kind="oracle",
+    return dict(value=n_tok / dt, unit="tokens/s", cores=cores, kind="oracle", cpu_model=cpu_model(),
                 sample=f"the same {n_tok} tokens as cpu_baseline, one contiguous token chunk per thread "
                        f"({cores} threads), {dt:.1f} s")
 
@@ -368,6 +420,14 @@ def main():
         if ev is not None:
             ev[3].record(stream)
 
+    # The plain-copy ceiling first (the reference the block's rates are read
+    # against); its ~40 ms of copies also take the GPU out of its idle clocks
+    # before the block's own warm-up.
+    copy_gbs, copy_figures = None, None
+    if not args.no_copy_ceiling:
+        print("bench: plain-copy ceiling", file=sys.stderr, flush=True)
+        copy_gbs, copy_figures = copy_ceiling(dev)
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -396,22 +456,6 @@ def main():
     eff_gbs = ab["block"] / (wall / args.steps) / 1e9
     dom = "ffn_fused"
     ach = ab[dom] / per[dom] / 1e9
-    copy_gbs = None
-    if not args.no_copy_ceiling:
-        # plain copy on the same device, 1 GiB read + 1 GiB write (also the
-        # reference dispatch for scaling the FETCH_SIZE / WRITE_SIZE counters)
-        src = torch.empty(1 << 29, dtype=torch.int16, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(10):
-            dst.copy_(src)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        copy_gbs = 2 * src.numel() * 2 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-        del src, dst
 
     # next row: RMSNorm + MXFP8 cast of the attention boundary's collapsed input
     # (cast only, the GEMM-ready operand), timed with HIP events on its own
@@ -442,7 +486,7 @@ def main():
                                "attention + FFN boundaries", "batch": 1, "seq_len": 4096,
                    "d": d, "hc": 4, "stream_dtype": "bf16", "input_sets": args.sets},
         "hbm_effective_gb_s": eff_gbs, "hbm_effective_pct_of_peak": 100 * eff_gbs / PEAK_HBM_GBS,
-        "copy_ceiling_gb_s": copy_gbs,
+        "copy_ceiling_gb_s": copy_gbs, "copy_figures_gb_s": copy_figures,
         "entry_point_us": {k: v * 1e6 for k, v in per.items()},
         "algorithmic_bytes": ab,
         "roofline": {"kernel": f"hc_fused_step, FFN boundary ({ENTRY_KERNELS[dom]})",

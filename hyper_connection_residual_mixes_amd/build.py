@@ -36,6 +36,12 @@ def build(out: str = LIB_PATH, extra_flags=(), sources=None) -> str:
     return out
 
 
+def build_bench_copy(out: str = os.path.join(ROOT, "bench_copy.so")) -> str:
+    """The benchmark's plain-copy reference kernel (bench_copy.hip at the repository
+    root), a library of its own: it is measurement, not part of the C ABI."""
+    return build(out=out, sources=[os.path.join(ROOT, "bench_copy.hip")])
+
+
 def build_host_sanitized(out: str) -> str:
     """The same library with AddressSanitizer and UndefinedBehaviorSanitizer on its
     host code only (the device code is built as usual); every finding aborts. For

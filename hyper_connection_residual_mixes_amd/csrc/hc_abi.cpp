@@ -32,6 +32,10 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 size_t elem_size(int dtype) { return dtype == HC_BF16 ? 2 : 4; }
 
+int64_t launch_items(int64_t n, int hc, int64_t d) {
+    return hc == kHC ? hc::max_launch_items(n, d) : hc::generic_max_launch_items(n, hc, d);
+}
+
 // Shape rules shared by the stream entry points. Returns HC_OK or an error.
 int check_shape(int64_t n, int hc, int64_t d, int dtype) {
     // d <= 2^20 keeps every per-wave byte offset of the kernels within 31 bits
@@ -40,6 +44,8 @@ int check_shape(int64_t n, int hc, int64_t d, int dtype) {
     if (hc < 1 || hc > hc::kMaxHC || d % 8 != 0) return HC_ERR_UNSUPPORTED;
     // every byte offset must fit comfortably in 63 bits
     if (n > 0 && (uint64_t)d > (uint64_t(1) << 40) / (uint64_t)n) return HC_ERR_SHAPE;
+    // every grid the launchers form must fit the launch limit
+    if (n > 0 && launch_items(n, hc, d) > hc::kMaxLaunchItems) return HC_ERR_SHAPE;
     return HC_OK;
 }
 
@@ -107,6 +113,8 @@ int hc_split_sinkhorn(const float* mixes, const float* hc_scale, const float* hc
                       int sinkhorn_iters, float eps, float* pre, float* post, float* comb, void* stream) {
     if (n < 0 || n > kMaxRows) return HC_ERR_SHAPE;
     if (hc < 1 || hc > hc::kMaxHC) return HC_ERR_UNSUPPORTED;
+    // a lane per token (four streams) or a wave per token (other counts)
+    if (hc != kHC && n > hc::kMaxLaunchItems / 64) return HC_ERR_SHAPE;
     if (sinkhorn_iters < 1 || check_eps(eps) != HC_OK) return HC_ERR_ARG;
     if (n == 0) return HC_OK;
     if (!mixes || !hc_scale || !hc_base || !pre || !post || !comb) return HC_ERR_NULL;

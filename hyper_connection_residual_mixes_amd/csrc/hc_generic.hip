@@ -909,6 +909,20 @@ hipError_t launch_projection(const void* x, bool bf16, int64_t n, int hc, int64_
 
 }  // namespace
 
+// Work-items of the largest grid the launchers of this file form for (n, hc, d):
+// the projection (both stream dtypes, with and without the collapse), the
+// finalize and split (a wave per token), and the collapse and expand (a wave per
+// token and 512 channels).
+int64_t generic_max_launch_items(int64_t n, int hc, int64_t d) {
+    int64_t m = ceil_div_g(n, kGBlock / 64) * kGBlock;
+    const int64_t ew = wave_grid(n, d) * kGBlock;
+    if (ew > m) m = ew;
+    const GenericPlan plans[] = {plan_f32(n, hc, d), plan_bf16(n, hc, d, false), plan_bf16(n, hc, d, true)};
+    for (const GenericPlan& p : plans)
+        if (p.tiles * p.nsplit * kGBlock > m) m = p.tiles * p.nsplit * kGBlock;
+    return m;
+}
+
 size_t generic_workspace_bytes(int64_t n, int hc, int64_t d) {
     return plan_generic(n, hc, d, true, true).total_bytes;
 }

@@ -22,6 +22,10 @@ struct PassPlan {
 PassPlan plan_pass(int64_t n, int64_t d, bool bf16);
 // Workspace that covers the plans of both stream dtypes.
 size_t workspace_bytes(int64_t n, int64_t d);
+// Work-items of the largest grid any four-stream launcher forms for (n, d); a
+// launch takes at most kMaxLaunchItems per dimension.
+int64_t max_launch_items(int64_t n, int64_t d);
+constexpr int64_t kMaxLaunchItems = (int64_t(1) << 32) - 1;
 
 struct PassRequest {
     const void* res;         // streams entering the boundary [n][4][d]
@@ -95,6 +99,7 @@ struct GenericRequest {
 };
 
 size_t generic_workspace_bytes(int64_t n, int hc, int64_t d);
+int64_t generic_max_launch_items(int64_t n, int hc, int64_t d);
 
 // Device address of the static no-allocation scratch (HC_NOALLOC_SCRATCH_BYTES)
 // on the device of `stream`; looked up once per device (hc_noalloc.hip).

@@ -794,12 +794,18 @@ __global__ __launch_bounds__(kFinBlock) void finalize_wave_kernel(FinalizeArgs f
     const int g = lane >> 3, q = lane & 7;
     const CoefParams cp = load_coef_params(f, lane & 15);
     const __amdgpu_buffer_rsrc_t r = make_rsrc(f.part, (int64_t)f.nsplit * f.n * kPart * (int64_t)sizeof(float));
+    // the rounds the slice count needs (uniform); the loads of the others are skipped
+    const int rounds = (f.nsplit + 7) / 8;
     float4 v[kFinWaveRounds];
 #pragma unroll
     for (int k = 0; k < kFinWaveRounds; ++k) {
-        const int64_t s = g + 8 * k;
-        const uint32_t off = s < f.nsplit ? (uint32_t)(((s * f.n + tt) * kPart + 4 * q) * sizeof(float)) : kOffMasked;
-        v[k] = buf_load16f(r, off, 0);
+        v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (k < rounds) {
+            const int64_t s = g + 8 * k;
+            const uint32_t off =
+                s < f.nsplit ? (uint32_t)(((s * f.n + tt) * kPart + 4 * q) * sizeof(float)) : kOffMasked;
+            v[k] = buf_load16f(r, off, 0);
+        }
     }
     float4 acc = v[0];
 #pragma unroll
@@ -1670,6 +1676,25 @@ PassPlan plan_pass(int64_t n, int64_t d, bool bf16) {
     // partial rows: nsplit x n x 32 floats
     p.workspace_bytes = (size_t)p.nsplit * (size_t)n * kPart * sizeof(float);
     return p;
+}
+
+// Work-items of the largest grid the four-stream launchers form for (n, d), over
+// every entry point and both stream dtypes: the split (a lane per token), the
+// collapse and expand (a lane per 8 channels), the sweeps, and the finalize (16
+// lanes per token, or a wave per token when there are more than 8 slices).
+int64_t max_launch_items(int64_t n, int64_t d) {
+    int64_t m = ceil_div(n, kSplitBlock) * kSplitBlock;
+    const int64_t ew = ceil_div(n * (d / 8), kEwBlock) * kEwBlock;
+    if (ew > m) m = ew;
+    for (int k = 0; k < 2; ++k) {
+        const PassPlan p = plan_pass(n, d, k == 1);
+        const int64_t sweep = p.tiles * p.nsplit * (k == 1 ? kSwBlock : kPassBlock);
+        const int64_t fin = p.nsplit > kFin16Slices ? ceil_div(n, kFinBlock / 64) * kFinBlock
+                                                    : ceil_div(n * 16, kFinBlock) * kFinBlock;
+        if (sweep > m) m = sweep;
+        if (fin > m) m = fin;
+    }
+    return m;
 }
 
 size_t workspace_bytes(int64_t n, int64_t d) {

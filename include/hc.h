@@ -35,8 +35,12 @@
  *     rounded to nearest, ties to even.
  *   - Supported sizes: 1 <= hc <= 8; 8 <= d <= 1048576 and d % 8 == 0;
  *     0 <= n < 2^31 (n == 0 is a no-op returning HC_OK without touching any
- *     pointer) and n * d <= 2^40. Larger n, d or n * d return HC_ERR_SHAPE
- *     (hc_split_sinkhorn takes the same bound on n). hc == 4 runs the
+ *     pointer) and n * d <= 2^40; and every kernel grid the call forms must
+ *     fit a launch (at most 2^32 - 1 work-items): with four streams that is
+ *     n < 2^28 and n * d <= 2^35, with other stream counts
+ *     n * ceil(d / 512) < 2^26. Larger sizes return HC_ERR_SHAPE before any
+ *     HIP call (hc_split_sinkhorn: n < 2^31 with four streams, n < 2^26
+ *     otherwise). hc == 4 runs the
  *     single-pass kernels; other stream counts run one kernel per step (the
  *     fused boundary as expand, projection, split, collapse in sequence).
  *   - Alignment: every tensor pointer (streams, sublayer input/output, hc_fn,

@@ -273,7 +273,65 @@ def test_fused_noalloc_validation():
     assert _fused_noalloc(n=1 << 40, d=1 << 20) == SHAPE
     assert hc.workspace_size(4096, 8, 5120) > 32 << 20
     assert _fused_noalloc(hc_=8, n=4096, d=5120) == -9
-    assert _fused_noalloc(n=262145, d=5120) == -9            # four streams: 128 B per token beyond 2^18
+    # the largest four-stream token count at d = 5120 whose workspace fits the buffer
+    lo, hi = 1, 1 << 22
+    while lo < hi:
+        mid = (lo + hi + 1) // 2
+        lo, hi = (mid, hi) if hc.workspace_size(mid, 4, 5120) <= 32 << 20 else (lo, mid - 1)
+    assert hc.workspace_size(lo + 1, 4, 5120) > 32 << 20
+    assert _fused_noalloc(n=lo + 1, d=5120) == -9
     # within the buffer, validation passes and the first HIP call (no GPU here) fails
-    assert _fused_noalloc(n=262144, d=5120, y=0x7000000000, pre=0x7100000000, post=0x7200000000,
+    assert _fused_noalloc(n=lo, d=5120, y=0x7000000000, pre=0x7100000000, post=0x7200000000,
                           comb=0x7300000000, pre_mix=0x7400000000, res=0x1000000000) == HIP
+
+
+def _largest_accepted(hc_, d):
+    """The largest token count hc_workspace_size accepts for (hc, d) (it returns 0
+    for a shape the entry points reject)."""
+    lo, hi = 0, (1 << 31) - 1
+    while lo < hi:
+        mid = (lo + hi + 1) // 2
+        lo, hi = (mid, hi) if hc.workspace_size(mid, hc_, d) > 0 else (lo, mid - 1)
+    return lo
+
+
+@pytest.mark.parametrize("hc_,d", [(4, 8), (4, 5120), (4, 1 << 20), (2, 8), (8, 5120), (3, 1 << 20)])
+def test_launch_grid_bounds(hc_, d):
+    """Every kernel grid must fit a launch (2^32 - 1 work-items per dimension). The
+    grids grow with the token count: with four streams the finalize takes 16 lanes
+    per token and the collapse/expand a lane per 8 channels; other stream counts
+    take a wave per token and per 512 channels. The documented limits follow, and
+    the entry points reject the first size beyond them before any HIP call."""
+    n = _largest_accepted(hc_, d)
+    limit = (1 << 32) - 1
+    grid = lambda lanes: -(-lanes // 256) * 256   # whole 256-thread workgroups
+    if hc_ == 4:
+        items = lambda m: max(grid(16 * m), grid(m * (d // 8)))
+        assert n < 1 << 28 and n * d <= 1 << 35
+    else:
+        items = lambda m: grid(64 * m * -(-d // 512))
+        assert n * -(-d // 512) < 1 << 26
+    assert items(n) <= limit < items(n + 1)
+    # the first rejected size, through every stream entry point (fake, far-apart pointers)
+    far = [(k + 1) << 42 for k in range(10)]
+    L = hc.lib()
+    m = n + 1
+    assert L.hc_pre(P(far[0]), 1, P(far[1]), m, hc_, d, P(far[2]), None) == SHAPE
+    assert L.hc_post(P(far[0]), P(far[1]), 1, P(far[2]), P(far[3]), m, hc_, d, P(far[4]), None) == SHAPE
+    assert L.hc_mixes(P(far[0]), 1, m, hc_, d, P(far[1]), 1e-20, P(far[2]), P(far[3]), 1 << 40, None) == SHAPE
+    assert L.hc_fused_step(P(far[0]), None, None, None, P(far[1]), P(far[2]), P(far[3]), P(far[3] + 64), m, hc_, d,
+                           1, 1e-20, 20, 1e-6, None, P(far[4]), P(far[5]), P(far[6]), P(far[7]), None, P(far[8]),
+                           1 << 40, None) == SHAPE
+    # at the largest accepted size, validation passes (the first HIP call fails: no GPU)
+    assert L.hc_pre(P(far[0]), 1, P(far[1]), n, hc_, d, P(far[2]), None) == HIP
+
+
+def test_split_grid_bound():
+    """The split takes a lane per token with four streams and a wave per token with
+    other stream counts."""
+    L = hc.lib()
+    big = (1 << 26) + 1
+    assert L.hc_split_sinkhorn(P(1 << 42), P(2 << 42), P(3 << 42), big, 8, 20, 1e-6, P(4 << 42), P(5 << 42),
+                               P(6 << 42), None) == SHAPE
+    assert L.hc_split_sinkhorn(P(1 << 42), P(2 << 42), P(3 << 42), big, 4, 20, 1e-6, P(4 << 42), P(5 << 42),
+                               P(6 << 42), None) == HIP
