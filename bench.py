@@ -89,21 +89,43 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def copy_ceiling(dev, nbytes: int = 1 << 30, reps: int = 10):
-    """The plain-copy reference (bench_copy.hip, a grid-stride copy of 16-byte
-    elements) on `nbytes` in + `nbytes` out, with cached and with non-temporal
-    stores at three grid sizes; HIP events on the launch stream, median of `reps`
-    after 3 warm-up copies. Returns (best GB/s, all figures)."""
+def _ceilings_lib():
     import ctypes
-    import statistics
-    import torch
-    path = os.path.join(ROOT, "bench_copy.so")
+    path = os.path.join(ROOT, "bench_ceilings.so")
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing (run __graft_entry__.build())")
     L = ctypes.CDLL(path)
     L.bench_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                              ctypes.c_void_p]
     L.bench_copy.restype = ctypes.c_int
+    L.bench_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    L.bench_mfma_bf16.restype = ctypes.c_int
+    return L
+
+
+def _median_seconds(run, stream, reps):
+    import statistics
+    import torch
+    for _ in range(3):
+        run()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e-3)
+    return statistics.median(times)
+
+
+def copy_ceiling(dev, nbytes: int = 1 << 30, reps: int = 10):
+    """The plain-copy reference (bench_ceilings.hip, a grid-stride copy of 16-byte
+    elements) on `nbytes` in + `nbytes` out, with cached and with non-temporal
+    stores at three grid sizes; HIP events on the launch stream, median of `reps`
+    after 3 warm-up copies. Returns (best GB/s, all figures)."""
+    import torch
+    L = _ceilings_lib()
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     src.fill_(1)
@@ -115,18 +137,30 @@ def copy_ceiling(dev, nbytes: int = 1 << 30, reps: int = 10):
                 rc = L.bench_copy(src.data_ptr(), dst.data_ptr(), nbytes, nt, wgs, stream.cuda_stream)
                 if rc != 0:
                     raise RuntimeError(f"bench_copy failed ({rc})")
-            for _ in range(3):
-                run()
-            times = []
-            for _ in range(reps):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                run()
-                e1.record(stream)
-                torch.cuda.synchronize()
-                times.append(e0.elapsed_time(e1) * 1e-3)
-            figures[f"{'nontemporal' if nt else 'cached'}_{wgs}wg"] = 2 * nbytes / statistics.median(times) / 1e9
+            figures[f"{'nontemporal' if nt else 'cached'}_{wgs}wg"] = 2 * nbytes / _median_seconds(run, stream,
+                                                                                                   reps) / 1e9
     del src, dst
+    return max(figures.values()), figures
+
+
+def mfma_ceiling(dev, iters: int = 2000, reps: int = 5):
+    """Sustained rate of v_mfma_f32_16x16x32_bf16 (bench_ceilings.hip: eight
+    independent accumulators per wave, no memory traffic), in TFLOP/s, at 1024
+    and 2048 workgroups of 4 waves; median of `reps`. Returns (best, all figures)."""
+    import torch
+    L = _ceilings_lib()
+    stream = torch.cuda.current_stream(dev)
+    figures = {}
+    for wgs in (1024, 2048):
+        out = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+
+        def run():
+            rc = L.bench_mfma_bf16(out.data_ptr(), out.numel() * 4, wgs, iters, stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"bench_mfma_bf16 failed ({rc})")
+        flops = wgs * 4 * iters * 8 * 16384
+        figures[f"{wgs}wg"] = flops / _median_seconds(run, stream, reps) / 1e12
+        del out
     return max(figures.values()), figures
 
 
@@ -423,10 +457,11 @@ def main():
     # The plain-copy ceiling first (the reference the block's rates are read
     # against); its ~40 ms of copies also take the GPU out of its idle clocks
     # before the block's own warm-up.
-    copy_gbs, copy_figures = None, None
+    copy_gbs, copy_figures, mfma_tf, mfma_figures = None, None, None, None
     if not args.no_copy_ceiling:
-        print("bench: plain-copy ceiling", file=sys.stderr, flush=True)
+        print("bench: plain-copy and MFMA ceilings", file=sys.stderr, flush=True)
         copy_gbs, copy_figures = copy_ceiling(dev)
+        mfma_tf, mfma_figures = mfma_ceiling(dev)
 
     for i in range(args.warmup):
         step(i)
@@ -487,6 +522,7 @@ def main():
                    "d": d, "hc": 4, "stream_dtype": "bf16", "input_sets": args.sets},
         "hbm_effective_gb_s": eff_gbs, "hbm_effective_pct_of_peak": 100 * eff_gbs / PEAK_HBM_GBS,
         "copy_ceiling_gb_s": copy_gbs, "copy_figures_gb_s": copy_figures,
+        "mfma_bf16_16x16x32_ceiling_tflop_s": mfma_tf, "mfma_figures_tflop_s": mfma_figures,
         "entry_point_us": {k: v * 1e6 for k, v in per.items()},
         "algorithmic_bytes": ab,
         "roofline": {"kernel": f"hc_fused_step, FFN boundary ({ENTRY_KERNELS[dom]})",

@@ -36,10 +36,11 @@ def build(out: str = LIB_PATH, extra_flags=(), sources=None) -> str:
     return out
 
 
-def build_bench_copy(out: str = os.path.join(ROOT, "bench_copy.so")) -> str:
-    """The benchmark's plain-copy reference kernel (bench_copy.hip at the repository
-    root), a library of its own: it is measurement, not part of the C ABI."""
-    return build(out=out, sources=[os.path.join(ROOT, "bench_copy.hip")])
+def build_bench_ceilings(out: str = os.path.join(ROOT, "bench_ceilings.so")) -> str:
+    """The benchmark's ceiling kernels (plain copy, MFMA rate: bench_ceilings.hip at
+    the repository root), a library of its own: it is measurement, not part of the
+    C ABI."""
+    return build(out=out, sources=[os.path.join(ROOT, "bench_ceilings.hip")])
 
 
 def build_host_sanitized(out: str) -> str:

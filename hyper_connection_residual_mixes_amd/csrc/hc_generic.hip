@@ -23,7 +23,11 @@
 //                           of 64 columns (fp32 streams).
 //   mixes_partial_bf16_kernel  the same partial rows for bf16 streams: 128 tokens
 //                           per workgroup, bf16 MFMAs on the exact stream values
-//                           and on the weights split into three bf16 terms.
+//                           and on the weights split into three bf16 terms
+//                           (one to three streams).
+//   mixes_wide_bf16_kernel  the same for five to eight bf16 streams: 256 tokens
+//                           per workgroup, staging and multiplying waves meeting
+//                           at one barrier per tile.
 //   mixes_finalize_kernel   a wave per token: partial rows summed over the slices
 //                           in order, scaled by the RMS statistic.
 //
@@ -699,6 +703,289 @@ void mixes_partial_bf16_kernel(const uint16_t* __restrict__ x, const float* __re
     }
 }
 
+// ---------------------------------------- wide projection (bf16, 5 to 8 streams)
+// Workgroup (tile, slice): 256 tokens t0 .. t0 + 255 and a slice of 64-channel
+// blocks, walked in the tiles of mixes_partial_bf16_kernel (block b of stream 0,
+// 1, ..., hc-1, then block b + 1); eight waves in two roles that meet at one
+// barrier per tile, through double-buffered LDS.
+//
+// Staging (waves 4-7, lane s = tid - 256): fetches each stream tile two tiles
+// ahead into registers (slot p: token row s / 8 + 32 p, channels 8 (s % 8) ..
+// +8), writes it to LDS as it is and accumulates the collapse (as
+// mixes_partial_bf16_kernel: ascending stream, one fma each, stored after the
+// block's last stream).
+//
+// Multiplying (waves 0-3, lane m = tid): wave w takes tokens 64 w .. 64 w + 63
+// (four row tiles) times every mix column tile, with the MFMA steps of
+// mixes_partial_bf16_kernel, so each weight plane read from LDS serves 64
+// tokens. Between their MFMAs these lanes also fetch the weight tiles two tiles
+// ahead (slot r: row m / 16 + 16 r, columns 4 (m % 16) .. +4) and write each,
+// split into three bf16 planes, to LDS one tile ahead: a weight tile is fetched
+// and split once per 256 tokens.
+constexpr int kWTok = 256;        // tokens per workgroup
+constexpr int kWThreads = 512;    // 4 multiplying + 4 staging waves
+constexpr int kWSlots = kWTok / 32;   // stream slots per staging lane
+
+__host__ __device__ constexpr int wide_lds_bytes(int R) { return 2 * (kWTok + 3 * 16 * R) * kBRow * 2; }
+
+template <bool kPre>
+struct WideX {
+    uint4 xw[kWSlots];
+    float pm[kPre ? kWSlots : 1];
+};
+
+template <bool kPre>
+__device__ __forceinline__ void wide_load_x(WideX<kPre>& st, const __amdgpu_buffer_rsrc_t (&xr)[kWSlots],
+                                            uint32_t xoff, const float* pre_mix, int64_t n, int hc, int64_t d,
+                                            int64_t t0, int64_t b, int j) {
+    const int s = threadIdx.x - 256;
+    const int64_t e0 = b * kGCols, c0 = (int64_t)j * d + e0;
+    const uint32_t xo = e0 + (s & 7) * 8 < d ? xoff : kOffMaskedG;   // d is a multiple of 8
+#pragma unroll
+    for (int p = 0; p < kWSlots; ++p) st.xw[p] = bload16(xr[p], xo, (uint32_t)(c0 * 2));
+    if constexpr (kPre) {
+#pragma unroll
+        for (int p = 0; p < kWSlots; ++p) {
+            const int64_t t = t0 + (s >> 3) + 32 * p;
+            st.pm[p] = t < n ? pre_mix[t * hc + j] : 0.f;
+        }
+    }
+}
+
+template <bool kPre>
+__device__ __forceinline__ void wide_store_x(const WideX<kPre>& st, uint16_t* xs,
+                                             float (&yacc)[kPre ? kWSlots : 1][8], uint16_t* __restrict__ y,
+                                             int64_t n, int hc, int64_t d, int64_t t0, int64_t b, int j) {
+    const int s = threadIdx.x - 256, col = (s & 7) * 8;
+#pragma unroll
+    for (int p = 0; p < kWSlots; ++p)
+        *reinterpret_cast<uint4*>(xs + ((s >> 3) + 32 * p) * kBRow + col) = st.xw[p];
+    if constexpr (kPre) {
+#pragma unroll
+        for (int p = 0; p < kWSlots; ++p) {
+            const uint32_t u[4] = {st.xw[p].x, st.xw[p].y, st.xw[p].z, st.xw[p].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                yacc[p][2 * q] = fmaf(st.pm[p], bf16_lo_g(u[q]), yacc[p][2 * q]);
+                yacc[p][2 * q + 1] = fmaf(st.pm[p], bf16_hi_g(u[q]), yacc[p][2 * q + 1]);
+            }
+        }
+        if (j == hc - 1) {
+            const int64_t e = b * kGCols + (s & 7) * 8;
+#pragma unroll
+            for (int p = 0; p < kWSlots; ++p) {
+                const int64_t t = t0 + (s >> 3) + 32 * p;
+                if (t < n && e < d)
+                    *reinterpret_cast<uint4*>(y + t * d + e) =
+                        make_uint4(pack2(yacc[p][0], yacc[p][1]), pack2(yacc[p][2], yacc[p][3]),
+                                   pack2(yacc[p][4], yacc[p][5]), pack2(yacc[p][6], yacc[p][7]));
+#pragma unroll
+                for (int i = 0; i < 8; ++i) yacc[p][i] = 0.f;
+            }
+        }
+    }
+}
+
+// Staging role: 1 + ntile barriers, as the multiplying role. Tile u sits in
+// register stage u % 2; tiles u + 2 and u + 3 are in flight while tile u is
+// multiplied.
+template <bool kPre>
+__device__ __forceinline__ void wide_stage_role(const uint16_t* __restrict__ x, const float* __restrict__ pre_mix,
+                                                int64_t n, int hc, int64_t d, int64_t t0, int64_t b_begin, int ntile,
+                                                uint16_t* xs, uint16_t* __restrict__ y) {
+    const int s = threadIdx.x - 256;
+    const int64_t K = (int64_t)hc * d;
+    __amdgpu_buffer_rsrc_t xr[kWSlots];
+#pragma unroll
+    for (int p = 0; p < kWSlots; ++p) {
+        const int64_t row0 = t0 + 32 * p;
+        xr[p] = rsrc_g(x + row0 * K, (n - row0) * K * 2);
+    }
+    const uint32_t xoff = (uint32_t)((int64_t)(s >> 3) * K * 2 + (s & 7) * 16);
+    float yacc[kPre ? kWSlots : 1][8];
+#pragma unroll
+    for (int p = 0; p < (kPre ? kWSlots : 1); ++p)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) yacc[p][i] = 0.f;
+    auto tile_bj = [&](int u, int64_t& b, int& j) {
+        const int q = u / hc;
+        b = b_begin + q;
+        j = u - q * hc;
+    };
+    auto load = [&](WideX<kPre>& st, int u) {
+        int64_t b;
+        int j;
+        tile_bj(u, b, j);
+        wide_load_x<kPre>(st, xr, xoff, pre_mix, n, hc, d, t0, b, j);
+    };
+    auto store = [&](const WideX<kPre>& st, uint16_t* buf, int u) {
+        int64_t b;
+        int j;
+        tile_bj(u, b, j);
+        wide_store_x<kPre>(st, buf, yacc, y, n, hc, d, t0, b, j);
+    };
+    constexpr int kXBuf = kWTok * kBRow;
+    WideX<kPre> st[2];
+    load(st[0], 0);
+    if (ntile > 1) load(st[1], 1);
+    store(st[0], xs, 0);
+    if (ntile > 2) load(st[0], 2);
+    __syncthreads();   // tile 0 is staged
+    for (int u0 = 0; u0 < ntile; u0 += 2) {
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+            const int u = u0 + sl;   // the tile being multiplied; u % 2 == sl
+            if (u < ntile) {
+                if (u + 1 < ntile) {
+                    store(st[1 - sl], xs + (1 - sl) * kXBuf, u + 1);
+                    if (u + 3 < ntile) load(st[1 - sl], u + 3);
+                }
+                __syncthreads();   // tile u is consumed, tile u + 1 is staged
+            }
+        }
+    }
+}
+
+template <int R>
+__device__ __forceinline__ void wide_load_w(uint4 (&wv)[R], const __amdgpu_buffer_rsrc_t (&wr)[R], uint32_t woff,
+                                            int64_t d, int64_t b, int j) {
+    const int m = threadIdx.x;
+    const int64_t e0 = b * kGCols, c0 = (int64_t)j * d + e0;
+    const uint32_t wo = e0 + (m & 15) * 4 < d ? woff : kOffMaskedG;
+#pragma unroll
+    for (int r = 0; r < R; ++r) wv[r] = bload16(wr[r], wo, (uint32_t)(c0 * 4));
+}
+
+template <int R>
+__device__ __forceinline__ void wide_store_w(const uint4 (&wv)[R], uint16_t* ws) {
+    const int m = threadIdx.x;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int i = (m >> 4) + 16 * r, lc = (m & 15) * 4;
+        uint32_t h0, m0, l0, h1, m1, l1;
+        split3_pair(__uint_as_float(wv[r].x), __uint_as_float(wv[r].y), h0, m0, l0);
+        split3_pair(__uint_as_float(wv[r].z), __uint_as_float(wv[r].w), h1, m1, l1);
+        uint16_t* row = ws + i * kBRow + lc;
+        *reinterpret_cast<uint2*>(row) = make_uint2(h0, h1);
+        *reinterpret_cast<uint2*>(row + 16 * R * kBRow) = make_uint2(m0, m1);
+        *reinterpret_cast<uint2*>(row + 32 * R * kBRow) = make_uint2(l0, l1);
+    }
+}
+
+template <int R>
+__device__ __forceinline__ void wide_mul_role(const float* __restrict__ hc_fn, int64_t n, int hc, int64_t d,
+                                              int64_t t0, int64_t b_begin, int ntile, int slice, const uint16_t* xs,
+                                              uint16_t* ws, float* __restrict__ part, int pg) {
+    constexpr int kBT = 4;
+    constexpr int kXBuf = kWTok * kBRow, kWBuf = 3 * 16 * R * kBRow;
+    const int M = (2 + hc) * hc;
+    const int64_t K = (int64_t)hc * d;
+    const int m = threadIdx.x, lane = m & 63, w = m >> 6;
+    const int r16 = lane & 15, g = lane >> 4;
+    __amdgpu_buffer_rsrc_t wr[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) wr[r] = rsrc_g(hc_fn + (int64_t)16 * r * K, (int64_t)(M - 16 * r) * K * 4);
+    const uint32_t woff = (uint32_t)((int64_t)(m >> 4) * K * 4 + (m & 15) * 16);
+    auto load = [&](uint4 (&wv)[R], int u) {
+        const int q = u / hc;
+        wide_load_w<R>(wv, wr, woff, d, b_begin + q, u - q * hc);
+    };
+    floatx4_g acc[kBT][R], gram[kBT];
+#pragma unroll
+    for (int T = 0; T < kBT; ++T) {
+        gram[T] = floatx4_g{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[T][r] = floatx4_g{0.f, 0.f, 0.f, 0.f};
+    }
+    uint4 wv[2][R];
+    load(wv[0], 0);
+    if (ntile > 1) load(wv[1], 1);
+    wide_store_w<R>(wv[0], ws);
+    if (ntile > 2) load(wv[0], 2);
+    __syncthreads();   // tile 0 is staged
+    for (int u0 = 0; u0 < ntile; u0 += 2) {
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+            const int u = u0 + sl;   // u % 2 == sl
+            if (u < ntile) {
+                if (u + 1 < ntile) {   // the next tile's weights, into the buffer tile u - 1 has freed
+                    wide_store_w<R>(wv[1 - sl], ws + (1 - sl) * kWBuf);
+                    if (u + 3 < ntile) load(wv[1 - sl], u + 3);
+                }
+                const uint16_t* xa = xs + sl * kXBuf + (w * 16 * kBT + r16) * kBRow + g * 8;
+                const uint16_t* wb = ws + sl * kWBuf + r16 * kBRow + g * 8;
+#pragma unroll
+                for (int kb = 0; kb < kGCols / 32; ++kb) {
+                    bf16x8_g a[kBT], bv[2][3];
+#pragma unroll
+                    for (int T = 0; T < kBT; ++T)
+                        a[T] = *reinterpret_cast<const bf16x8_g*>(xa + T * 16 * kBRow + kb * 32);
+#pragma unroll
+                    for (int plane = 0; plane < 3; ++plane)
+                        bv[0][plane] = *reinterpret_cast<const bf16x8_g*>(wb + plane * 16 * R * kBRow + kb * 32);
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        if (r + 1 < R) {
+#pragma unroll
+                            for (int plane = 0; plane < 3; ++plane)
+                                bv[(r + 1) & 1][plane] = *reinterpret_cast<const bf16x8_g*>(
+                                    wb + ((r + 1) * 16 + plane * 16 * R) * kBRow + kb * 32);
+                        }
+#pragma unroll
+                        for (int plane = 0; plane < 3; ++plane)
+#pragma unroll
+                            for (int T = 0; T < kBT; ++T)
+                                acc[T][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[T], bv[r & 1][plane],
+                                                                                    acc[T][r], 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int T = 0; T < kBT; ++T)
+                        gram[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[T], a[T], gram[T], 0, 0, 0);
+                }
+                __syncthreads();   // tile u is consumed, tile u + 1 is staged
+            }
+        }
+    }
+    // accumulator lane l of row tile T: tokens 64 w + 16 T + 4 g + i, mix 16 r + r16
+#pragma unroll
+    for (int T = 0; T < kBT; ++T) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int mix = r * 16 + r16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t t = t0 + w * 16 * kBT + T * 16 + 4 * g + i;
+                if (t < n && mix < M) part[((int64_t)slice * n + t) * pg + mix] = acc[T][r][i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t t = t0 + w * 16 * kBT + T * 16 + r16;
+            if (r16 == 4 * g + i && t < n) part[((int64_t)slice * n + t) * pg + M] = gram[T][i];
+        }
+    }
+}
+
+template <int R, bool kPre>
+__global__ __launch_bounds__(kWThreads, 1)
+void mixes_wide_bf16_kernel(const uint16_t* __restrict__ x, const float* __restrict__ hc_fn, int64_t n, int hc,
+                            int64_t d, int blk_per_split, int nsplit, float* __restrict__ part, int pg,
+                            const float* __restrict__ pre_mix, uint16_t* __restrict__ y) {
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2 * kWTok * kBRow];
+    __shared__ __attribute__((aligned(16))) uint16_t ws[2 * 3 * 16 * R * kBRow];
+    const int64_t tile = blockIdx.x / nsplit;
+    const int slice = (int)(blockIdx.x - tile * nsplit);
+    const int64_t t0 = tile * kWTok;
+    const int64_t nblk = (d + kGCols - 1) / kGCols;
+    const int64_t b_begin = (int64_t)slice * blk_per_split;
+    const int64_t b_end = b_begin + blk_per_split < nblk ? b_begin + blk_per_split : nblk;
+    const int ntile = (int)(b_end - b_begin) * hc;   // >= hc: slices are never empty
+    if (__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) >= 4)   // wave-uniform role
+        wide_stage_role<kPre>(x, pre_mix, n, hc, d, t0, b_begin, ntile, xs, y);
+    else
+        wide_mul_role<R>(hc_fn, n, hc, d, t0, b_begin, ntile, slice, xs, ws, part, pg);
+}
+
 // A wave per token: lane l sums entries l and l + 64 of the partial rows over the
 // slices in order, then scales the dots by 1 / sqrt(sum of squares / (hc d) + eps).
 // Token t's mixes from its partial rows: lane l gets mixes l (a0) and l + 64 (a1),
@@ -808,10 +1095,27 @@ GenericPlan plan_bf16(int64_t n, int hc, int64_t d, bool pre) {
     return p;
 }
 
+// bf16 streams, five to eight (wide kernel): 256-token tiles x slices of 64-channel
+// blocks, one workgroup per CU (its LDS), 256 CUs.
+bool use_wide(int hc) { return hc >= 5; }
+
+GenericPlan plan_wide(int64_t n, int64_t d) {
+    GenericPlan p{};
+    const int64_t nblk = ceil_div_g(d, kGCols);
+    p.tiles = ceil_div_g(n, kWTok);
+    int64_t ns = ceil_div_g(256, p.tiles);
+    if (ns > nblk) ns = nblk;
+    if (ns > kGMaxSplit) ns = kGMaxSplit;
+    if (ns < 1) ns = 1;
+    p.per_split = (int)ceil_div_g(nblk, ns);
+    p.nsplit = (int)ceil_div_g(nblk, p.per_split);
+    return p;
+}
+
 // The workspace layout does not depend on the stream dtype or on the collapse:
 // room for the partial rows of the largest plan, then the scratch mixes.
 GenericPlan plan_generic(int64_t n, int hc, int64_t d, bool bf16, bool pre) {
-    GenericPlan p = bf16 ? plan_bf16(n, hc, d, pre) : plan_f32(n, hc, d);
+    GenericPlan p = bf16 ? (use_wide(hc) ? plan_wide(n, d) : plan_bf16(n, hc, d, pre)) : plan_f32(n, hc, d);
     const int M = (2 + hc) * hc;
     p.pg = (M + 1 + 3) & ~3;
     int ns_max = plan_f32(n, hc, d).nsplit;
@@ -819,6 +1123,7 @@ GenericPlan plan_generic(int64_t n, int hc, int64_t d, bool bf16, bool pre) {
         const int ns = plan_bf16(n, hc, d, q == 1).nsplit;
         if (ns > ns_max) ns_max = ns;
     }
+    if (use_wide(hc) && plan_wide(n, d).nsplit > ns_max) ns_max = plan_wide(n, d).nsplit;
     p.mixes_offset = ((size_t)ns_max * (size_t)n * (size_t)p.pg * sizeof(float) + 255) & ~size_t(255);
     p.total_bytes = p.mixes_offset + (size_t)n * (size_t)M * sizeof(float);
     return p;
@@ -862,6 +1167,24 @@ void launch_partial_bf16_t(const GenericPlan& p, const uint16_t* x, const float*
     }
 }
 
+template <int R, bool kPre>
+void launch_wide_v(const GenericPlan& p, const uint16_t* x, const float* hc_fn, int64_t n, int hc, int64_t d,
+                   float* part, const float* pre_mix, uint16_t* y, hipStream_t stream) {
+    static_assert(wide_lds_bytes(R) <= 160 * 1024, "LDS of one CU");
+    hipLaunchKernelGGL((mixes_wide_bf16_kernel<R, kPre>), dim3((unsigned)(p.tiles * p.nsplit)), dim3(kWThreads), 0,
+                       stream, x, hc_fn, n, hc, d, p.per_split, p.nsplit, part, p.pg, pre_mix, y);
+}
+
+template <bool kPre>
+void launch_wide(const GenericPlan& p, const uint16_t* x, const float* hc_fn, int64_t n, int hc, int64_t d,
+                 float* part, const float* pre_mix, uint16_t* y, hipStream_t stream) {
+    switch ((2 + hc) * hc) {
+        case 80: launch_wide_v<5, kPre>(p, x, hc_fn, n, hc, d, part, pre_mix, y, stream); break;   // hc = 8
+        case 63: launch_wide_v<4, kPre>(p, x, hc_fn, n, hc, d, part, pre_mix, y, stream); break;   // hc = 7
+        default: launch_wide_v<3, kPre>(p, x, hc_fn, n, hc, d, part, pre_mix, y, stream); break;   // hc = 5, 6
+    }
+}
+
 // The projection's partial rows (with the collapse when y is given), then the
 // finalize into `mixes`.
 struct SplitArgs {   // the split fused into the finalize launch
@@ -881,7 +1204,13 @@ hipError_t launch_projection(const void* x, bool bf16, int64_t n, int hc, int64_
                              hipStream_t stream, const SplitArgs* sp = nullptr) {
     const GenericPlan p = plan_generic(n, hc, d, bf16, y != nullptr);
     float* part = static_cast<float*>(workspace);
-    if (bf16) {
+    if (bf16 && use_wide(hc)) {
+        const uint16_t* xb = static_cast<const uint16_t*>(x);
+        if (y)
+            launch_wide<true>(p, xb, hc_fn, n, hc, d, part, pre_mix, static_cast<uint16_t*>(y), stream);
+        else
+            launch_wide<false>(p, xb, hc_fn, n, hc, d, part, nullptr, nullptr, stream);
+    } else if (bf16) {
         const uint16_t* xb = static_cast<const uint16_t*>(x);
         if (y)
             launch_partial_bf16_t<true>(p, xb, hc_fn, n, hc, d, part, pre_mix, static_cast<uint16_t*>(y), stream);
@@ -920,6 +1249,10 @@ int64_t generic_max_launch_items(int64_t n, int hc, int64_t d) {
     const GenericPlan plans[] = {plan_f32(n, hc, d), plan_bf16(n, hc, d, false), plan_bf16(n, hc, d, true)};
     for (const GenericPlan& p : plans)
         if (p.tiles * p.nsplit * kGBlock > m) m = p.tiles * p.nsplit * kGBlock;
+    if (use_wide(hc)) {
+        const GenericPlan p = plan_wide(n, d);
+        if (p.tiles * p.nsplit * kWThreads > m) m = p.tiles * p.nsplit * kWThreads;
+    }
     return m;
 }
 
@@ -979,6 +1312,7 @@ hipError_t launch_mixes_generic(const void* x, bool bf16, int64_t n, int hc, int
 // finalize + split (one launch) -> collapse (fp32 streams)
 hipError_t launch_fused_generic(const GenericRequest& r, hipStream_t stream) {
     const bool fused_pre = r.bf16 && r.y;
+    const SplitArgs sp{r.scale, r.base, r.iters, r.eps, r.pre, r.post, r.comb};
     const void* src = r.res;
     if (r.f_prev) {
         if (hipError_t e = launch_post_generic(r.f_prev, r.res, r.bf16, r.post_prev, r.comb_prev, r.n, r.hc, r.d,
@@ -988,7 +1322,6 @@ hipError_t launch_fused_generic(const GenericRequest& r, hipStream_t stream) {
         src = r.streams_out;
     }
     // the finalize splits the mixes in the same launch; they are stored only when asked for
-    const SplitArgs sp{r.scale, r.base, r.iters, r.eps, r.pre, r.post, r.comb};
     if (hipError_t e = launch_projection(src, r.bf16, r.n, r.hc, r.d, r.hc_fn, r.norm_eps, r.mixes, r.workspace,
                                          fused_pre ? r.pre_mix : nullptr, fused_pre ? r.y : nullptr, stream, &sp);
         e != hipSuccess)

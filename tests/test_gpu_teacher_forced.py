@@ -18,7 +18,8 @@ dropped in the expand instances of the sweeps.
 
 Cases: every instance of the bf16 sweep with the expand (64-token and 128-token
 groups, with and without the collapse), the fp32 pass, the full decode and
-prefill FFN boundaries, ragged token counts and widths.
+prefill FFN boundaries, ragged token counts and widths; for five to eight streams,
+the boundary with the wide (256-token) projection after the expand.
 """
 import pytest
 import torch
@@ -61,7 +62,7 @@ def _block_boundary(inp):
     """The FFN boundary of a block: the oracle's attention coefficients (post, comb,
     pre) are the previous-sublayer inputs both sides receive."""
     x = inp["x"]
-    _, preA, postA, combA = oracle.hc_mixes_split(x, *inp["attn"])
+    _, preA, postA, combA = oracle.hc_mixes_split(x, *inp["attn"], hc_mult=x.shape[-2])
     return x, inp["ffn"], inp["f_attn"], postA, combA, preA
 
 
@@ -96,6 +97,49 @@ def test_in_place_expand():
     inp = hc_inputs.block_inputs(w, seed=14, outlier_frac=0.02, scale_mode="uniform")
     x, ffn, f, post, comb, pi = _block_boundary(inp)
     got = teacher_forced_boundary("out of place", x, ffn, f, post, comb, pi)
+    xd = to_dev(x)
+    got2 = hc.hc_fused_step(xd, *to_dev(ffn), pre_mix=to_dev(pi), f_prev=to_dev(f), post_prev=to_dev(post),
+                            comb_prev=to_dev(comb), streams_out=xd, want_mixes=True)
+    torch.cuda.synchronize()
+    assert torch.equal(xd.cpu(), got["streams"].cpu())
+    for k in ("y", "mixes", "pre", "post", "comb"):
+        assert torch.equal(got2[k].cpu(), got[k].cpu()), k
+
+
+@pytest.mark.parametrize("hc_", [5, 6, 7, 8])
+@pytest.mark.parametrize("n,d", [(130, 1288), (64, 5120), (3, 8), (600, 264)])
+@pytest.mark.parametrize("collapse", [True, False])
+def test_generic_expand_boundary(hc_, n, d, collapse):
+    """Five to eight bf16 streams: the expand, then the wide projection of the rounded
+    x1. Ragged token counts (partial 256-token tiles) and widths (a partial last
+    64-channel block; d = 8 a single partial block)."""
+    w = hc_inputs.Workload(f"tf_hc{hc_}_{n}x{d}", 1, n, d, torch.bfloat16, hc=hc_)
+    inp = hc_inputs.block_inputs(w, seed=15 + hc_, outlier_frac=0.05, scale_mode="uniform")
+    x, ffn, f, post, comb, pi = _block_boundary(inp)
+    teacher_forced_boundary(f"hc={hc_} {n}x{d}", x, ffn, f, post, comb, pi if collapse else None)
+
+
+def test_generic_expand_boundary_full_size_in_place():
+    """Eight streams at the prefill size (4096 tokens x 5120, 1% x50 outliers: the
+    launch configuration the benchmark times), teacher-forced on 48 sampled tokens;
+    then the same call in place over the residual, bit-identical."""
+    w = hc_inputs.Workload("tf_hc8_prefill", 1, 4096, 5120, torch.bfloat16, hc=8)
+    inp = hc_inputs.block_inputs(w, seed=16, outlier_frac=0.01)
+    # previous coefficients from the oracle's split of the drawn logits (no projection of 4096 tokens)
+    pi, post, comb = oracle.hc_split_sinkhorn(*inp["prev"], hc_mult=8)
+    x, ffn, f = inp["x"], inp["ffn"], inp["f_attn"]
+    got = hc.hc_fused_step(*to_dev((x,)), *to_dev(ffn), pre_mix=to_dev(pi), f_prev=to_dev(f),
+                           post_prev=to_dev(post), comb_prev=to_dev(comb), want_mixes=True)
+    torch.cuda.synchronize()
+    sample = torch.randperm(w.n, generator=hc_inputs.generator(12))[:48].sort().values
+    x1 = got["streams"][sample.to(DEV)].cpu()
+    check("hc=8 prefill x1 (sampled, same inputs)", x1,
+          oracle.hc_post(f[sample], x[sample], post[sample], comb[sample]), TOL_BF16)
+    ref = oracle.fused_step(x1, *ffn, pre_mix=pi[sample])
+    for k in ("mixes", "pre", "post", "comb"):
+        check(f"hc=8 prefill {k} (sampled, GPU x1)", got[k][sample.to(DEV)].cpu(), ref[k], TOL_F32,
+              rho=rho_for(k))
+    check("hc=8 prefill y (sampled, GPU x1)", got["y"][sample.to(DEV)].cpu(), ref["y"], TOL_BF16)
     xd = to_dev(x)
     got2 = hc.hc_fused_step(xd, *to_dev(ffn), pre_mix=to_dev(pi), f_prev=to_dev(f), post_prev=to_dev(post),
                             comb_prev=to_dev(comb), streams_out=xd, want_mixes=True)
