@@ -5,7 +5,7 @@ The GPU tests append one line per comparison to the file named by HC_PARITY_LOG
 script reads such a log and prints, per tolerance, the checks closest to their
 bound, and the worst teacher-forced error per output kind.
 
-    python tests/margin_summary.py gpurun_out/margins.tsv > tests/parity_margins.md
+    python tests/margin_summary.py gpurun_out/parity_log.tsv "<the pytest command>" > tests/parity_margins.md
 """
 import sys
 from collections import defaultdict
