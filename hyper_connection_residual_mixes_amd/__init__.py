@@ -113,7 +113,7 @@ def _size(t: torch.Tensor, count: int, what: str, device) -> torch.Tensor:
     faulting the GPU."""
     if t.numel() != count:
         raise ValueError(f"{what} must hold {count} elements, got {t.numel()} (shape {tuple(t.shape)})")
-    if t.device != device:
+    if t.get_device() != device.index:
         raise ValueError(f"{what} is on {t.device}, expected {device}")
     return t
 
@@ -316,8 +316,7 @@ def _fused_step(residual, hc_fn, hc_scale, hc_base, pre_mix, f_prev, post_prev, 
         mixes = None
     args = (_ptr(residual), _ptr(f_prev), _ptr(post_prev) if expand else None,
             _ptr(comb_prev) if expand else None, _ptr(pre_mix) if want_y else None,
-            _ptr(_dev(hc_fn, "hc_fn", torch.float32)), _ptr(_dev(hc_scale, "hc_scale", torch.float32)),
-            _ptr(_dev(hc_base, "hc_base", torch.float32)), n, hc, d, _dtype_code(residual),
+            _ptr(hc_fn), _ptr(hc_scale), _ptr(hc_base), n, hc, d, _dtype_code(residual),
             float(norm_eps), int(sinkhorn_iters), float(eps), _ptr(streams_out) if expand else None,
             _ptr(y), _ptr(pre), _ptr(post), _ptr(comb), _ptr(mixes))
     if noalloc:
