@@ -98,8 +98,8 @@ def _ceilings_lib():
     L.bench_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                              ctypes.c_void_p]
     L.bench_copy.restype = ctypes.c_int
-    L.bench_stream_mix.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
-                                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    L.bench_stream_mix.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     L.bench_stream_mix.restype = ctypes.c_int
     L.bench_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     L.bench_mfma_bf16.restype = ctypes.c_int
@@ -123,10 +123,10 @@ def _median_seconds(run, stream, reps):
 
 
 def copy_ceiling(dev, nbytes: int = 1 << 30, reps: int = 10):
-    """The plain-copy reference (bench_ceilings.hip, a grid-stride copy of 16-byte
-    elements) on `nbytes` in + `nbytes` out, with cached and with non-temporal
-    stores at three grid sizes; HIP events on the launch stream, median of `reps`
-    after 3 warm-up copies. Returns (best GB/s, all figures)."""
+    """The plain-copy reference (bench_ceilings.hip, a copy of 16-byte elements) on
+    `nbytes` in + `nbytes` out, with cached and with non-temporal stores, one element
+    per lane and grid-stride at three grid sizes; HIP events on the launch stream,
+    median of `reps` after 3 warm-up copies. Returns (best GB/s, all figures)."""
     import torch
     L = _ceilings_lib()
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -135,12 +135,12 @@ def copy_ceiling(dev, nbytes: int = 1 << 30, reps: int = 10):
     stream = torch.cuda.current_stream(dev)
     figures = {}
     for nt in (0, 1):
-        for wgs in (1024, 2048, 4096):
+        for wgs in (0, 1024, 2048, 4096):
             def run():
                 rc = L.bench_copy(src.data_ptr(), dst.data_ptr(), nbytes, nt, wgs, stream.cuda_stream)
                 if rc != 0:
                     raise RuntimeError(f"bench_copy failed ({rc})")
-            figures[f"{'nontemporal' if nt else 'cached'}_{wgs}wg"] = 2 * nbytes / _median_seconds(run, stream,
+            figures[f"{'nontemporal' if nt else 'cached'}_{wgs or 'one_shot'}wg"] = 2 * nbytes / _median_seconds(run, stream,
                                                                                                    reps) / 1e9
     del src, dst
     return max(figures.values()), figures
@@ -150,35 +150,40 @@ STREAM_MIXES = (("read_4", 4, 0), ("attention_flow_4r_1w", 4, 1), ("ffn_flow_5r_
                 ("expand_flow_5r_4w", 5, 4))
 
 
-def stream_mix_ceilings(dev, plane_bytes: int = 4096 * 5120 * 2, reps: int = 10):
-    """Plain streaming with the block's read/write mixes (bench_ceilings.hip: planes of
-    one 4096 x 5120 bf16 stream each, combined element by element in address order),
-    cached and non-temporal stores, 2048 workgroups. Three sets of planes rotate so
-    that no call finds its inputs in the 256 MB last-level cache. Returns GB/s per mix."""
+def stream_mix_ceilings(dev, rows: int = 4096, row_bytes: int = 5120 * 2, reps: int = 10):
+    """Plain streaming with the block's read/write mixes (bench_ceilings.hip: rows of
+    4096 tokens, each holding its planes of one 5120-channel bf16 stream back to back,
+    as the streams are laid out), cached and non-temporal stores, one element per
+    lane and grid-stride at 512 and 1024 workgroups. Three sets rotate so that no call finds its inputs in the 256 MB
+    last-level cache. Returns (best GB/s per mix, all figures)."""
     import torch
     L = _ceilings_lib()
     stream = torch.cuda.current_stream(dev)
-    src = torch.empty(3 * 5 * plane_bytes, dtype=torch.uint8, device=dev)
-    dst = torch.empty(3 * 5 * plane_bytes, dtype=torch.uint8, device=dev)
+    set_bytes = rows * 5 * row_bytes
+    src = torch.empty(3 * set_bytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty(3 * set_bytes, dtype=torch.uint8, device=dev)
     src.fill_(1)
-    out = {}
+    best, figures = {}, {}
     for name, nr, nw in STREAM_MIXES:
         for nt in (0, 1):
             if nw == 0 and nt:
                 continue
-            k = [0]
+            key = f"{name}{'_nontemporal' if nt else ''}"
+            for wgs in (0, 512, 1024):
+                k = [0]
 
-            def run():
-                s = k[0] % 3
-                k[0] += 1
-                rc = L.bench_stream_mix(src.data_ptr() + s * 5 * plane_bytes, dst.data_ptr() + s * 5 * plane_bytes,
-                                        plane_bytes, nr, nw, nt, 2048, stream.cuda_stream)
-                if rc != 0:
-                    raise RuntimeError(f"bench_stream_mix failed ({rc})")
-            sec = _median_seconds(run, stream, reps)
-            out[f"{name}{'_nontemporal' if nt else ''}"] = (nr + nw) * plane_bytes / sec / 1e9
+                def run():
+                    s = k[0] % 3
+                    k[0] += 1
+                    rc = L.bench_stream_mix(src.data_ptr() + s * set_bytes, dst.data_ptr() + s * set_bytes, rows,
+                                            row_bytes, nr, nw, nt, wgs, stream.cuda_stream)
+                    if rc != 0:
+                        raise RuntimeError(f"bench_stream_mix failed ({rc})")
+                gbs = (nr + nw) * rows * row_bytes / _median_seconds(run, stream, reps) / 1e9
+                figures[f"{key}_{wgs or 'one_shot'}wg"] = gbs
+                best[key] = max(best.get(key, 0.0), gbs)
     del src, dst
-    return out
+    return best, figures
 
 
 def mfma_ceiling(dev, iters: int = 2000, reps: int = 5):
@@ -495,11 +500,11 @@ def main():
     # The plain-copy ceiling first (the reference the block's rates are read
     # against); its ~40 ms of copies also take the GPU out of its idle clocks
     # before the block's own warm-up.
-    copy_gbs, copy_figures, mix_figures, mfma_tf, mfma_figures = None, None, None, None, None
+    copy_gbs, copy_figures, mix_best, mix_figures, mfma_tf, mfma_figures = None, None, None, None, None, None
     if not args.no_copy_ceiling:
         print("bench: plain-copy and MFMA ceilings", file=sys.stderr, flush=True)
         copy_gbs, copy_figures = copy_ceiling(dev)
-        mix_figures = stream_mix_ceilings(dev)
+        mix_best, mix_figures = stream_mix_ceilings(dev)
         mfma_tf, mfma_figures = mfma_ceiling(dev)
 
     for i in range(args.warmup):
@@ -561,7 +566,7 @@ def main():
                    "d": d, "hc": 4, "stream_dtype": "bf16", "input_sets": args.sets},
         "hbm_effective_gb_s": eff_gbs, "hbm_effective_pct_of_peak": 100 * eff_gbs / PEAK_HBM_GBS,
         "copy_ceiling_gb_s": copy_gbs, "copy_figures_gb_s": copy_figures,
-        "stream_mix_ceilings_gb_s": mix_figures,
+        "stream_mix_ceilings_gb_s": mix_best, "stream_mix_figures_gb_s": mix_figures,
         "mfma_bf16_16x16x32_ceiling_tflop_s": mfma_tf, "mfma_figures_tflop_s": mfma_figures,
         "entry_point_us": {k: v * 1e6 for k, v in per.items()},
         "algorithmic_bytes": ab,
