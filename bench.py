@@ -326,10 +326,11 @@ def decode_latency(dev, reps: int = 300):
             "algorithmic_bytes": block_bytes, "achieved_gb_s_graph": block_bytes / graph_wall / 1e9}
 
 
-def generic_hc_blocks(dev, steps: int = 10):
+def generic_hc_blocks(dev, steps: int = 20, warmup: int = 20):
     """The prefill block (4096 tokens x hc streams x 5120 bf16) at stream counts
     other than four, which run one kernel per step; timed with HIP events around
-    `steps` blocks after a warm-up."""
+    `steps` blocks after `warmup` blocks (with 2 warm-up blocks the GPU's clocks were
+    still rising: 534-541 us at hc = 8 against 494-495 us after 100)."""
     import torch
     import hc_inputs
     import hyper_connection_residual_mixes_amd as hc
@@ -347,7 +348,7 @@ def generic_hc_blocks(dev, steps: int = 10):
             hc.block(inp["x"], pi, inp["attn"], inp["ffn"], inp["f_attn"], inp["f_ffn"], x1_out=x1, x2_out=x2,
                      workspace=ws)
 
-        for _ in range(2):
+        for _ in range(warmup):
             step()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
