@@ -706,60 +706,88 @@ void mixes_partial_bf16_kernel(const uint16_t* __restrict__ x, const float* __re
 // ---------------------------------------- wide projection (bf16, 5 to 8 streams)
 // Workgroup (tile, slice): 256 tokens t0 .. t0 + 255 and a slice of 64-channel
 // blocks, walked in the tiles of mixes_partial_bf16_kernel (block b of stream 0,
-// 1, ..., hc-1, then block b + 1); eight waves in two roles that meet at one
+// 1, ..., hc-1, then block b + 1); twelve waves in two roles that meet at one
 // barrier per tile, through double-buffered LDS.
 //
-// Staging (waves 4-7, lane s = tid - 256): fetches each stream tile two tiles
-// ahead into registers (slot p: token row s / 8 + 32 p, channels 8 (s % 8) ..
-// +8), writes it to LDS as it is and accumulates the collapse (as
-// mixes_partial_bf16_kernel: ascending stream, one fma each, stored after the
-// block's last stream).
+// Staging (waves 4-11, lane s = tid - 256 of 512): fetches each tile two tiles
+// ahead into registers (stream slot p: token row s / 8 + 64 p, channels 8 (s % 8)
+// .. +8; weight slot r: row s / 16 + 32 r, columns 4 (s % 16) .. +4), writes the
+// stream tile to LDS as it is and the weights split into three bf16 planes, and
+// accumulates the collapse (as mixes_partial_bf16_kernel: ascending stream, one
+// fma each, stored after the block's last stream).
 //
-// Multiplying (waves 0-3, lane m = tid): wave w takes tokens 64 w .. 64 w + 63
-// (four row tiles) times every mix column tile, with the MFMA steps of
-// mixes_partial_bf16_kernel, so each weight plane read from LDS serves 64
-// tokens. Between their MFMAs these lanes also fetch the weight tiles two tiles
-// ahead (slot r: row m / 16 + 16 r, columns 4 (m % 16) .. +4) and write each,
-// split into three bf16 planes, to LDS one tile ahead: a weight tile is fetched
-// and split once per 256 tokens.
+// Multiplying (waves 0-3): wave w takes tokens 64 w .. 64 w + 63 (four row
+// tiles) times every mix column tile, with the MFMA steps of
+// mixes_partial_bf16_kernel; each weight plane read from LDS serves 64 tokens,
+// and a weight tile is fetched and split once per 256 tokens. These waves do
+// nothing but LDS reads and MFMAs: the projection at five to eight streams is
+// bound by MFMA issue, so the staging work runs on the other eight waves, beside
+// it on the same SIMDs.
 constexpr int kWTok = 256;        // tokens per workgroup
-constexpr int kWThreads = 512;    // 4 multiplying + 4 staging waves
-constexpr int kWSlots = kWTok / 32;   // stream slots per staging lane
+constexpr int kWThreads = 768;    // 4 multiplying + 8 staging waves
+constexpr int kWStage = kWThreads - 256;      // staging lanes
+constexpr int kWSlots = kWTok * 8 / kWStage;  // stream slots per staging lane (4)
 
 __host__ __device__ constexpr int wide_lds_bytes(int R) { return 2 * (kWTok + 3 * 16 * R) * kBRow * 2; }
+__host__ __device__ constexpr int wide_w_slots(int R) { return (16 * R + 31) / 32; }   // weight slots per lane
 
-template <bool kPre>
-struct WideX {
+template <int R, bool kPre>
+struct WideStage {
     uint4 xw[kWSlots];
+    uint4 wv[wide_w_slots(R)];
     float pm[kPre ? kWSlots : 1];
 };
 
-template <bool kPre>
-__device__ __forceinline__ void wide_load_x(WideX<kPre>& st, const __amdgpu_buffer_rsrc_t (&xr)[kWSlots],
-                                            uint32_t xoff, const float* pre_mix, int64_t n, int hc, int64_t d,
-                                            int64_t t0, int64_t b, int j) {
+template <int R>
+struct WideSrc {
+    __amdgpu_buffer_rsrc_t x[kWSlots];
+    __amdgpu_buffer_rsrc_t w[wide_w_slots(R)];
+    uint32_t xoff, woff;
+};
+
+template <int R, bool kPre>
+__device__ __forceinline__ void wide_load(WideStage<R, kPre>& st, const WideSrc<R>& src, const float* pre_mix,
+                                          int64_t n, int hc, int64_t d, int64_t t0, int64_t b, int j) {
     const int s = threadIdx.x - 256;
     const int64_t e0 = b * kGCols, c0 = (int64_t)j * d + e0;
-    const uint32_t xo = e0 + (s & 7) * 8 < d ? xoff : kOffMaskedG;   // d is a multiple of 8
+    const uint32_t xo = e0 + (s & 7) * 8 < d ? src.xoff : kOffMaskedG;   // d is a multiple of 8
+    const uint32_t wo = e0 + (s & 15) * 4 < d ? src.woff : kOffMaskedG;
 #pragma unroll
-    for (int p = 0; p < kWSlots; ++p) st.xw[p] = bload16(xr[p], xo, (uint32_t)(c0 * 2));
+    for (int p = 0; p < kWSlots; ++p) st.xw[p] = bload16(src.x[p], xo, (uint32_t)(c0 * 2));
+#pragma unroll
+    for (int r = 0; r < wide_w_slots(R); ++r) st.wv[r] = bload16(src.w[r], wo, (uint32_t)(c0 * 4));
     if constexpr (kPre) {
 #pragma unroll
         for (int p = 0; p < kWSlots; ++p) {
-            const int64_t t = t0 + (s >> 3) + 32 * p;
+            const int64_t t = t0 + (s >> 3) + 64 * p;
             st.pm[p] = t < n ? pre_mix[t * hc + j] : 0.f;
         }
     }
 }
 
-template <bool kPre>
-__device__ __forceinline__ void wide_store_x(const WideX<kPre>& st, uint16_t* xs,
-                                             float (&yacc)[kPre ? kWSlots : 1][8], uint16_t* __restrict__ y,
-                                             int64_t n, int hc, int64_t d, int64_t t0, int64_t b, int j) {
+// Writes tile (b, j) to LDS buffers xs / ws and adds it to the collapse; the
+// collapse of block b is stored after its last stream.
+template <int R, bool kPre>
+__device__ __forceinline__ void wide_store(const WideStage<R, kPre>& st, uint16_t* xs, uint16_t* ws,
+                                           float (&yacc)[kPre ? kWSlots : 1][8], uint16_t* __restrict__ y,
+                                           int64_t n, int hc, int64_t d, int64_t t0, int64_t b, int j) {
     const int s = threadIdx.x - 256, col = (s & 7) * 8;
 #pragma unroll
     for (int p = 0; p < kWSlots; ++p)
-        *reinterpret_cast<uint4*>(xs + ((s >> 3) + 32 * p) * kBRow + col) = st.xw[p];
+        *reinterpret_cast<uint4*>(xs + ((s >> 3) + 64 * p) * kBRow + col) = st.xw[p];
+#pragma unroll
+    for (int r = 0; r < wide_w_slots(R); ++r) {
+        const int i = (s >> 4) + 32 * r, lc = (s & 15) * 4;
+        if (16 * R % 32 == 0 || i < 16 * R) {   // the last slot may run past the tile's rows
+            uint32_t h0, m0, l0, h1, m1, l1;
+            split3_pair(__uint_as_float(st.wv[r].x), __uint_as_float(st.wv[r].y), h0, m0, l0);
+            split3_pair(__uint_as_float(st.wv[r].z), __uint_as_float(st.wv[r].w), h1, m1, l1);
+            uint16_t* row = ws + i * kBRow + lc;
+            *reinterpret_cast<uint2*>(row) = make_uint2(h0, h1);
+            *reinterpret_cast<uint2*>(row + 16 * R * kBRow) = make_uint2(m0, m1);
+            *reinterpret_cast<uint2*>(row + 32 * R * kBRow) = make_uint2(l0, l1);
+        }
+    }
     if constexpr (kPre) {
 #pragma unroll
         for (int p = 0; p < kWSlots; ++p) {
@@ -774,7 +802,7 @@ __device__ __forceinline__ void wide_store_x(const WideX<kPre>& st, uint16_t* xs
             const int64_t e = b * kGCols + (s & 7) * 8;
 #pragma unroll
             for (int p = 0; p < kWSlots; ++p) {
-                const int64_t t = t0 + (s >> 3) + 32 * p;
+                const int64_t t = t0 + (s >> 3) + 64 * p;
                 if (t < n && e < d)
                     *reinterpret_cast<uint4*>(y + t * d + e) =
                         make_uint4(pack2(yacc[p][0], yacc[p][1]), pack2(yacc[p][2], yacc[p][3]),
@@ -789,19 +817,26 @@ __device__ __forceinline__ void wide_store_x(const WideX<kPre>& st, uint16_t* xs
 // Staging role: 1 + ntile barriers, as the multiplying role. Tile u sits in
 // register stage u % 2; tiles u + 2 and u + 3 are in flight while tile u is
 // multiplied.
-template <bool kPre>
-__device__ __forceinline__ void wide_stage_role(const uint16_t* __restrict__ x, const float* __restrict__ pre_mix,
-                                                int64_t n, int hc, int64_t d, int64_t t0, int64_t b_begin, int ntile,
-                                                uint16_t* xs, uint16_t* __restrict__ y) {
+template <int R, bool kPre>
+__device__ __forceinline__ void wide_stage_role(const uint16_t* __restrict__ x, const float* __restrict__ hc_fn,
+                                                const float* __restrict__ pre_mix, int64_t n, int hc, int64_t d,
+                                                int64_t t0, int64_t b_begin, int ntile, uint16_t* xs, uint16_t* ws,
+                                                uint16_t* __restrict__ y) {
     const int s = threadIdx.x - 256;
+    const int M = (2 + hc) * hc;
     const int64_t K = (int64_t)hc * d;
-    __amdgpu_buffer_rsrc_t xr[kWSlots];
+    WideSrc<R> src;
 #pragma unroll
     for (int p = 0; p < kWSlots; ++p) {
-        const int64_t row0 = t0 + 32 * p;
-        xr[p] = rsrc_g(x + row0 * K, (n - row0) * K * 2);
+        const int64_t row0 = t0 + 64 * p;
+        src.x[p] = rsrc_g(x + row0 * K, (n - row0) * K * 2);
     }
-    const uint32_t xoff = (uint32_t)((int64_t)(s >> 3) * K * 2 + (s & 7) * 16);
+#pragma unroll
+    for (int r = 0; r < wide_w_slots(R); ++r)
+        src.w[r] = rsrc_g(hc_fn + (int64_t)32 * r * K, (int64_t)(M - 32 * r) * K * 4);
+    src.xoff = (uint32_t)((int64_t)(s >> 3) * K * 2 + (s & 7) * 16);
+    src.woff = (uint32_t)((int64_t)(s >> 4) * K * 4 + (s & 15) * 16);
+    constexpr int kXBuf = kWTok * kBRow, kWBuf = 3 * 16 * R * kBRow;
     float yacc[kPre ? kWSlots : 1][8];
 #pragma unroll
     for (int p = 0; p < (kPre ? kWSlots : 1); ++p)
@@ -812,24 +847,21 @@ __device__ __forceinline__ void wide_stage_role(const uint16_t* __restrict__ x, 
         b = b_begin + q;
         j = u - q * hc;
     };
-    auto load = [&](WideX<kPre>& st, int u) {
-        int64_t b;
-        int j;
-        tile_bj(u, b, j);
-        wide_load_x<kPre>(st, xr, xoff, pre_mix, n, hc, d, t0, b, j);
-    };
-    auto store = [&](const WideX<kPre>& st, uint16_t* buf, int u) {
-        int64_t b;
-        int j;
-        tile_bj(u, b, j);
-        wide_store_x<kPre>(st, buf, yacc, y, n, hc, d, t0, b, j);
-    };
-    constexpr int kXBuf = kWTok * kBRow;
-    WideX<kPre> st[2];
-    load(st[0], 0);
-    if (ntile > 1) load(st[1], 1);
-    store(st[0], xs, 0);
-    if (ntile > 2) load(st[0], 2);
+    WideStage<R, kPre> st[2];
+    int64_t b;
+    int j;
+    tile_bj(0, b, j);
+    wide_load<R, kPre>(st[0], src, pre_mix, n, hc, d, t0, b, j);
+    if (ntile > 1) {
+        tile_bj(1, b, j);
+        wide_load<R, kPre>(st[1], src, pre_mix, n, hc, d, t0, b, j);
+    }
+    tile_bj(0, b, j);
+    wide_store<R, kPre>(st[0], xs, ws, yacc, y, n, hc, d, t0, b, j);
+    if (ntile > 2) {
+        tile_bj(2, b, j);
+        wide_load<R, kPre>(st[0], src, pre_mix, n, hc, d, t0, b, j);
+    }
     __syncthreads();   // tile 0 is staged
     for (int u0 = 0; u0 < ntile; u0 += 2) {
 #pragma unroll
@@ -837,8 +869,13 @@ __device__ __forceinline__ void wide_stage_role(const uint16_t* __restrict__ x, 
             const int u = u0 + sl;   // the tile being multiplied; u % 2 == sl
             if (u < ntile) {
                 if (u + 1 < ntile) {
-                    store(st[1 - sl], xs + (1 - sl) * kXBuf, u + 1);
-                    if (u + 3 < ntile) load(st[1 - sl], u + 3);
+                    tile_bj(u + 1, b, j);
+                    wide_store<R, kPre>(st[1 - sl], xs + (1 - sl) * kXBuf, ws + (1 - sl) * kWBuf, yacc, y, n, hc,
+                                        d, t0, b, j);
+                    if (u + 3 < ntile) {
+                        tile_bj(u + 3, b, j);
+                        wide_load<R, kPre>(st[1 - sl], src, pre_mix, n, hc, d, t0, b, j);
+                    }
                 }
                 __syncthreads();   // tile u is consumed, tile u + 1 is staged
             }
@@ -847,49 +884,13 @@ __device__ __forceinline__ void wide_stage_role(const uint16_t* __restrict__ x, 
 }
 
 template <int R>
-__device__ __forceinline__ void wide_load_w(uint4 (&wv)[R], const __amdgpu_buffer_rsrc_t (&wr)[R], uint32_t woff,
-                                            int64_t d, int64_t b, int j) {
-    const int m = threadIdx.x;
-    const int64_t e0 = b * kGCols, c0 = (int64_t)j * d + e0;
-    const uint32_t wo = e0 + (m & 15) * 4 < d ? woff : kOffMaskedG;
-#pragma unroll
-    for (int r = 0; r < R; ++r) wv[r] = bload16(wr[r], wo, (uint32_t)(c0 * 4));
-}
-
-template <int R>
-__device__ __forceinline__ void wide_store_w(const uint4 (&wv)[R], uint16_t* ws) {
-    const int m = threadIdx.x;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int i = (m >> 4) + 16 * r, lc = (m & 15) * 4;
-        uint32_t h0, m0, l0, h1, m1, l1;
-        split3_pair(__uint_as_float(wv[r].x), __uint_as_float(wv[r].y), h0, m0, l0);
-        split3_pair(__uint_as_float(wv[r].z), __uint_as_float(wv[r].w), h1, m1, l1);
-        uint16_t* row = ws + i * kBRow + lc;
-        *reinterpret_cast<uint2*>(row) = make_uint2(h0, h1);
-        *reinterpret_cast<uint2*>(row + 16 * R * kBRow) = make_uint2(m0, m1);
-        *reinterpret_cast<uint2*>(row + 32 * R * kBRow) = make_uint2(l0, l1);
-    }
-}
-
-template <int R>
-__device__ __forceinline__ void wide_mul_role(const float* __restrict__ hc_fn, int64_t n, int hc, int64_t d,
-                                              int64_t t0, int64_t b_begin, int ntile, int slice, const uint16_t* xs,
-                                              uint16_t* ws, float* __restrict__ part, int pg) {
+__device__ __forceinline__ void wide_mul_role(int64_t n, int hc, int64_t t0, int ntile, int slice, const uint16_t* xs,
+                                              const uint16_t* ws, float* __restrict__ part, int pg) {
     constexpr int kBT = 4;
     constexpr int kXBuf = kWTok * kBRow, kWBuf = 3 * 16 * R * kBRow;
     const int M = (2 + hc) * hc;
-    const int64_t K = (int64_t)hc * d;
-    const int m = threadIdx.x, lane = m & 63, w = m >> 6;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r16 = lane & 15, g = lane >> 4;
-    __amdgpu_buffer_rsrc_t wr[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) wr[r] = rsrc_g(hc_fn + (int64_t)16 * r * K, (int64_t)(M - 16 * r) * K * 4);
-    const uint32_t woff = (uint32_t)((int64_t)(m >> 4) * K * 4 + (m & 15) * 16);
-    auto load = [&](uint4 (&wv)[R], int u) {
-        const int q = u / hc;
-        wide_load_w<R>(wv, wr, woff, d, b_begin + q, u - q * hc);
-    };
     floatx4_g acc[kBT][R], gram[kBT];
 #pragma unroll
     for (int T = 0; T < kBT; ++T) {
@@ -897,54 +898,39 @@ __device__ __forceinline__ void wide_mul_role(const float* __restrict__ hc_fn, i
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[T][r] = floatx4_g{0.f, 0.f, 0.f, 0.f};
     }
-    uint4 wv[2][R];
-    load(wv[0], 0);
-    if (ntile > 1) load(wv[1], 1);
-    wide_store_w<R>(wv[0], ws);
-    if (ntile > 2) load(wv[0], 2);
     __syncthreads();   // tile 0 is staged
-    for (int u0 = 0; u0 < ntile; u0 += 2) {
+    for (int u = 0; u < ntile; ++u) {
+        const uint16_t* xa = xs + (u & 1) * kXBuf + (w * 16 * kBT + r16) * kBRow + g * 8;
+        const uint16_t* wb = ws + (u & 1) * kWBuf + r16 * kBRow + g * 8;
 #pragma unroll
-        for (int sl = 0; sl < 2; ++sl) {
-            const int u = u0 + sl;   // u % 2 == sl
-            if (u < ntile) {
-                if (u + 1 < ntile) {   // the next tile's weights, into the buffer tile u - 1 has freed
-                    wide_store_w<R>(wv[1 - sl], ws + (1 - sl) * kWBuf);
-                    if (u + 3 < ntile) load(wv[1 - sl], u + 3);
-                }
-                const uint16_t* xa = xs + sl * kXBuf + (w * 16 * kBT + r16) * kBRow + g * 8;
-                const uint16_t* wb = ws + sl * kWBuf + r16 * kBRow + g * 8;
+        for (int kb = 0; kb < kGCols / 32; ++kb) {
+            bf16x8_g a[kBT], bv[2][3];
 #pragma unroll
-                for (int kb = 0; kb < kGCols / 32; ++kb) {
-                    bf16x8_g a[kBT], bv[2][3];
+            for (int T = 0; T < kBT; ++T)
+                a[T] = *reinterpret_cast<const bf16x8_g*>(xa + T * 16 * kBRow + kb * 32);
 #pragma unroll
-                    for (int T = 0; T < kBT; ++T)
-                        a[T] = *reinterpret_cast<const bf16x8_g*>(xa + T * 16 * kBRow + kb * 32);
+            for (int plane = 0; plane < 3; ++plane)
+                bv[0][plane] = *reinterpret_cast<const bf16x8_g*>(wb + plane * 16 * R * kBRow + kb * 32);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                if (r + 1 < R) {
 #pragma unroll
                     for (int plane = 0; plane < 3; ++plane)
-                        bv[0][plane] = *reinterpret_cast<const bf16x8_g*>(wb + plane * 16 * R * kBRow + kb * 32);
+                        bv[(r + 1) & 1][plane] = *reinterpret_cast<const bf16x8_g*>(
+                            wb + ((r + 1) * 16 + plane * 16 * R) * kBRow + kb * 32);
+                }
 #pragma unroll
-                    for (int r = 0; r < R; ++r) {
-                        if (r + 1 < R) {
-#pragma unroll
-                            for (int plane = 0; plane < 3; ++plane)
-                                bv[(r + 1) & 1][plane] = *reinterpret_cast<const bf16x8_g*>(
-                                    wb + ((r + 1) * 16 + plane * 16 * R) * kBRow + kb * 32);
-                        }
-#pragma unroll
-                        for (int plane = 0; plane < 3; ++plane)
-#pragma unroll
-                            for (int T = 0; T < kBT; ++T)
-                                acc[T][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[T], bv[r & 1][plane],
-                                                                                    acc[T][r], 0, 0, 0);
-                    }
+                for (int plane = 0; plane < 3; ++plane)
 #pragma unroll
                     for (int T = 0; T < kBT; ++T)
-                        gram[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[T], a[T], gram[T], 0, 0, 0);
-                }
-                __syncthreads();   // tile u is consumed, tile u + 1 is staged
+                        acc[T][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[T], bv[r & 1][plane], acc[T][r], 0,
+                                                                            0, 0);
             }
+#pragma unroll
+            for (int T = 0; T < kBT; ++T)
+                gram[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[T], a[T], gram[T], 0, 0, 0);
         }
+        __syncthreads();   // tile u is consumed, tile u + 1 is staged
     }
     // accumulator lane l of row tile T: tokens 64 w + 16 T + 4 g + i, mix 16 r + r16
 #pragma unroll
@@ -981,9 +967,9 @@ void mixes_wide_bf16_kernel(const uint16_t* __restrict__ x, const float* __restr
     const int64_t b_end = b_begin + blk_per_split < nblk ? b_begin + blk_per_split : nblk;
     const int ntile = (int)(b_end - b_begin) * hc;   // >= hc: slices are never empty
     if (__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) >= 4)   // wave-uniform role
-        wide_stage_role<kPre>(x, pre_mix, n, hc, d, t0, b_begin, ntile, xs, y);
+        wide_stage_role<R, kPre>(x, hc_fn, pre_mix, n, hc, d, t0, b_begin, ntile, xs, ws, y);
     else
-        wide_mul_role<R>(hc_fn, n, hc, d, t0, b_begin, ntile, slice, xs, ws, part, pg);
+        wide_mul_role<R>(n, hc, t0, ntile, slice, xs, ws, part, pg);
 }
 
 // A wave per token: lane l sums entries l and l + 64 of the partial rows over the
