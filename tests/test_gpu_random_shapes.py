@@ -52,10 +52,12 @@ def test_block_random_wide_sweep(n, d, seed):
 
 
 # The widest supported stream, d = 2^20: the largest per-lane and per-row byte
-# offsets the kernels form (the single-pass sweeps, the fp32 pass and the generic
-# bf16 projection), a few tokens each so the oracle stays within seconds.
+# offsets the kernels form (the single-pass sweeps, the fp32 pass, the generic bf16
+# projection and the wide projection of five to eight streams, whose weight rows
+# are then 2^23 floats), a few tokens each so the oracle stays within seconds.
 @pytest.mark.parametrize("hc_,n,dtype,seed", [(4, 3, torch.bfloat16, 900), (4, 2, torch.float32, 901),
-                                              (2, 3, torch.bfloat16, 902), (2, 3, torch.float32, 903)])
+                                              (2, 3, torch.bfloat16, 902), (2, 3, torch.float32, 903),
+                                              (8, 2, torch.bfloat16, 904), (5, 3, torch.bfloat16, 905)])
 def test_block_max_width(hc_, n, dtype, seed):
     _block_case(hc_, n, 1 << 20, dtype, 20, seed)
 
