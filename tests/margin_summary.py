@@ -12,10 +12,14 @@ from collections import defaultdict
 
 
 def main(path: str, command: str) -> None:
-    rows = []
+    rows, reported = [], []
     for line in open(path):
-        test, name, err, tol = line.rstrip("\n").split("\t")
-        rows.append((test.split("::", 1)[-1], test.split("::", 1)[0], name, float(err), float(tol)))
+        f = line.rstrip("\n").split("\t")
+        test, name, err, tol = f[:4]
+        # report-only figures: marked in the fifth column (older logs: the chained end-to-end checks)
+        report = f[4] == "report" if len(f) > 4 else name.startswith("chained")
+        (reported if report else rows).append((test.split("::", 1)[-1], test.split("::", 1)[0], name, float(err),
+                                               float(tol)))
     print("# Parity margins of the GPU tests")
     print()
     print("Worst relative error of every comparison in one run of the GPU parity tests,")
@@ -23,9 +27,18 @@ def main(path: str, command: str) -> None:
     print()
     print(f"Command: `{command}`")
     print()
-    print(f"{len(rows)} comparisons, {len({r[0] for r in rows})} test cases, "
+    print(f"{len(rows)} gated comparisons, {len({r[0] for r in rows})} test cases, "
           f"worst ratio to tolerance {max(r[3] / r[4] for r in rows):.3f}.")
     print()
+    if reported:
+        print("Reported, not gated (the long-prefill chain end to end: the oracle's own chain over 80")
+        print("sublayers against the GPU's; the test holds these to its divergence guard instead):")
+        print()
+        print("| rel. error | ratio to the bf16 tolerance | test | check |")
+        print("|---|---|---|---|")
+        for r in sorted(reported, key=lambda r: -r[3]):
+            print(f"| {r[3]:.3e} | {r[3] / r[4]:.3f} | `{r[0]}` | {r[2]} |")
+        print()
     print("## Teacher-forced checks (the oracle fed the GPU's own inputs of the step)")
     print()
     print("| output | worst rel. error | tolerance | ratio | where |")

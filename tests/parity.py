@@ -44,16 +44,16 @@ def max_rel_err(got: torch.Tensor, ref: torch.Tensor, rho="row", tokens_dims=1) 
 
 def record(name: str, err: float, tol: float, gate: bool = True) -> float:
     """Prints a comparison's worst error, appends it to the margin log named by the
-    HC_PARITY_LOG environment variable (test id, name, error, tolerance; tab
-    separated), and asserts it is within the tolerance (unless gate is False: a
-    figure that is reported, not held to the tolerance)."""
+    HC_PARITY_LOG environment variable (test id, name, error, tolerance, "gate" or
+    "report"; tab separated), and asserts it is within the tolerance (unless gate is
+    False: a figure that is reported, not held to the tolerance)."""
     print(f"  {name:<28s} max rel err {err:.3e} (tol {tol:g})", flush=True)
     sys.stdout.flush()
     log = os.environ.get("HC_PARITY_LOG")
     if log:
         test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
         with open(log, "a") as fh:
-            fh.write(f"{test}\t{name}\t{err:.6e}\t{tol:g}\n")
+            fh.write(f"{test}\t{name}\t{err:.6e}\t{tol:g}\t{'gate' if gate else 'report'}\n")
     assert err <= tol or not gate, f"{name}: max relative error {err:.3e} > {tol:g}"
     return err
 
