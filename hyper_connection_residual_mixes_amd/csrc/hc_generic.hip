@@ -47,7 +47,10 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 constexpr int kGBlock = 256;
 constexpr int kGTok = 64;       // tokens per projection workgroup (16 per wave)
 constexpr int kGCols = 64;      // flattened columns per LDS tile
-constexpr int kGMaxSplit = 64;  // slices of the flattened axis
+// Slices of the flattened axis, at most. Few tokens take many slices: that fills
+// the GPU and keeps each slice's fp32 accumulation chain short (at d = 2^20 and
+// eight streams, 256 slices leave 32768 flattened columns per chain).
+constexpr int kGMaxSplit = 256;
 
 __device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
