@@ -101,6 +101,8 @@ def _ceilings_lib():
     L.bench_stream_mix.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     L.bench_stream_mix.restype = ctypes.c_int
+    L.bench_empty.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    L.bench_empty.restype = ctypes.c_int
     L.bench_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     L.bench_mfma_bf16.restype = ctypes.c_int
     return L
@@ -319,10 +321,29 @@ def decode_latency(dev, reps: int = 300):
     e1.record()
     torch.cuda.synchronize()
     graph_wall = (time.perf_counter() - t0) / (reps // 3 * 3)
+    # The launch floor of the same chain: five dependent empty kernels with the block's
+    # launch shapes (sweep, finalize, sweep, finalize, expand), replayed from a graph.
+    L = _ceilings_lib()
+    shapes = ((80, 512), (16, 256), (80, 512), (16, 256), (160, 256))
+    ge = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(ge):
+        for _ in range(3):
+            for wgs, threads in shapes:
+                if L.bench_empty(wgs, threads, torch.cuda.current_stream(dev).cuda_stream) != 0:
+                    raise RuntimeError("bench_empty failed")
+    for _ in range(20):
+        ge.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps // 3):
+        ge.replay()
+    torch.cuda.synchronize()
+    floor = (time.perf_counter() - t0) / (reps // 3 * 3)
     block_bytes = algorithmic_bytes(n, d)["block"]
     return {"workload": f"decode block, {n} tokens x 4 streams x {d} bf16 (attention + FFN boundaries)",
             "us_per_block_eager": eager_wall * 1e6, "us_per_block_eager_gpu": eager_gpu * 1e6,
             "us_per_block_graph": graph_wall * 1e6, "tokens_per_s_graph": n / graph_wall,
+            "launch_floor_us_per_block_graph": floor * 1e6,
             "algorithmic_bytes": block_bytes, "achieved_gb_s_graph": block_bytes / graph_wall / 1e9}
 
 

@@ -17,6 +17,9 @@
 // attention boundary's, the FFN boundary's and the expand's flows without their
 // arithmetic or their token-tiled walk.
 //
+// bench_empty: a kernel that does nothing, for the launch floor of a chain of
+// dependent launches (the decode block replayed from a graph).
+//
 // bench_mfma_bf16: back-to-back v_mfma_f32_16x16x32_bf16 (the instruction the
 // projections use), eight independent accumulators per wave, no memory traffic
 // inside the loop: the rate the matrix cores sustain for that instruction.
@@ -35,6 +38,8 @@
 //     (16-byte aligned, row_bytes a multiple of 16); 1 <= nread <= 5,
 //     0 <= nwrite <= 5; with nwrite = 0 nothing is written (the loads are kept by
 //     a comparison that never holds for the data the benchmark writes: all bytes 1).
+//   int bench_empty(int workgroups, int threads, void* stream)
+//     1 <= workgroups <= 2^20, 64 <= threads <= 1024 (a multiple of 64).
 //   int bench_mfma_bf16(float* out, int64_t out_bytes, int workgroups, int iters,
 //                       void* stream)
 //     out: device buffer of at least workgroups * 256 floats (one sum per lane,
@@ -108,6 +113,8 @@ int launch_mix_r(const u32x4_t* src, u32x4_t* dst, int64_t rows, int64_t row_ele
     return (int)hipGetLastError();
 }
 
+__global__ __launch_bounds__(1024) void empty_kernel() {}
+
 __global__ __launch_bounds__(256) void mfma_kernel(float* __restrict__ out, int iters) {
     bf16x8_t a, b;
     for (int i = 0; i < 8; ++i) {
@@ -176,4 +183,10 @@ extern "C" int bench_stream_mix(const void* src, void* dst, int64_t rows, int64_
         case 4: return launch_mix_r<4>(s, d, rows, row_elems, nwrite, nt, workgroups, st);
         default: return launch_mix_r<5>(s, d, rows, row_elems, nwrite, nt, workgroups, st);
     }
+}
+
+extern "C" int bench_empty(int workgroups, int threads, void* stream) {
+    if (workgroups < 1 || workgroups > (1 << 20) || threads < 64 || threads > 1024 || threads % 64 != 0) return -1;
+    hipLaunchKernelGGL(empty_kernel, dim3(workgroups), dim3(threads), 0, static_cast<hipStream_t>(stream));
+    return (int)hipGetLastError();
 }
