@@ -22,7 +22,11 @@
 //
 // bench_mfma_bf16: back-to-back v_mfma_f32_16x16x32_bf16 (the instruction the
 // projections use), eight independent accumulators per wave, no memory traffic
-// inside the loop: the rate the matrix cores sustain for that instruction.
+// inside the loop: the rate the matrix cores sustain for that instruction. The
+// file is built with the MFMA results in ordinary VGPRs (the build passes
+// -amdgpu-mfma-vgpr-form): in the accumulation-register form the compiler
+// rotates the eight accumulators through moves between the MFMAs of every
+// iteration, which waits on each result and halves the measured rate.
 //
 // Built by __graft_entry__.build() into bench_ceilings.so; C ABI:
 //   int bench_copy(const void* src, void* dst, int64_t bytes, int nontemporal,

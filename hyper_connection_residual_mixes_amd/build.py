@@ -36,11 +36,16 @@ def build(out: str = LIB_PATH, extra_flags=(), sources=None) -> str:
     return out
 
 
+# The MFMA-rate loop keeps its accumulators in VGPRs; in the accumulation-register
+# form the compiler moves them between registers around every MFMA.
+CEILINGS_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+
+
 def build_bench_ceilings(out: str = os.path.join(ROOT, "bench_ceilings.so")) -> str:
     """The benchmark's ceiling kernels (plain copy, MFMA rate: bench_ceilings.hip at
     the repository root), a library of its own: it is measurement, not part of the
     C ABI."""
-    return build(out=out, sources=[os.path.join(ROOT, "bench_ceilings.hip")])
+    return build(out=out, extra_flags=CEILINGS_FLAGS, sources=[os.path.join(ROOT, "bench_ceilings.hip")])
 
 
 def build_host_sanitized(out: str) -> str:

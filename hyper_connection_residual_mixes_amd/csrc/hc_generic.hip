@@ -723,9 +723,8 @@ void mixes_partial_bf16_kernel(const uint16_t* __restrict__ x, const float* __re
 // tiles) times every mix column tile, with the MFMA steps of
 // mixes_partial_bf16_kernel; each weight plane read from LDS serves 64 tokens,
 // and a weight tile is fetched and split once per 256 tokens. These waves do
-// nothing but LDS reads and MFMAs: the projection at five to eight streams is
-// bound by MFMA issue, so the staging work runs on the other eight waves, beside
-// it on the same SIMDs.
+// nothing but LDS reads and MFMAs; the staging work runs on the other eight
+// waves, beside them on the same SIMDs.
 constexpr int kWTok = 256;        // tokens per workgroup
 constexpr int kWThreads = 768;    // 4 multiplying + 8 staging waves
 constexpr int kWStage = kWThreads - 256;      // staging lanes
