@@ -16,7 +16,8 @@
 //                           eight streams).
 //   pre_generic_kernel      collapse, one lane per (token, 8 channels), a wave
 //                           per token and 512 channels.
-//   post_generic_kernel     expand + combine, the same mapping.
+//   post_generic_kernel     expand + combine, the same mapping; in a fused step
+//                           with an expand it also collapses the new streams.
 //   mixes_partial_kernel    64 tokens x one slice of the flattened hc*d axis per
 //                           workgroup: the (2+hc)*hc partial dot products (fp32
 //                           MFMA) and the partial sum of squares, from LDS tiles
@@ -273,16 +274,37 @@ __global__ __launch_bounds__(kGBlock) void pre_generic_kernel(const void* __rest
     store8<kBf16>(y, t * d + e, acc);
 }
 
+// The values a store8 of v writes, read back as fp32.
+template <bool kBf16>
+__device__ __forceinline__ void stored8(const float (&v)[8], float (&r)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (kBf16) {
+            const uint32_t w = pack2(v[2 * i], v[2 * i + 1]);
+            r[2 * i] = __uint_as_float(w << 16);
+            r[2 * i + 1] = __uint_as_float(w & 0xffff0000u);
+        } else {
+            r[2 * i] = v[2 * i];
+            r[2 * i + 1] = v[2 * i + 1];
+        }
+    }
+}
+
 // Every stream of the lane's 8 channels is read before any is written, so the
-// output may be the residual itself.
-template <bool kBf16, bool kStream>
+// output may be the residual itself. kCollapse: the new streams, as stored, are
+// also collapsed with pre_mix into y (ascending stream, one fma each, as the
+// collapse of the projection kernels and pre_generic_kernel do).
+template <bool kBf16, bool kStream, bool kCollapse>
 __global__ __launch_bounds__(kGBlock) void post_generic_kernel(const void* __restrict__ f, const void* res,
                                                                const float* __restrict__ post,
                                                                const float* __restrict__ comb, int64_t n, int hc,
-                                                               int64_t d, void* out) {
+                                                               int64_t d, void* out, const float* __restrict__ pre_mix,
+                                                               void* __restrict__ y) {
     int64_t t, e;
     if (!wave_token(n, d >> 3, t, e)) return;
-    float fv[8], rv[kMaxHC][8];
+    float fv[8], rv[kMaxHC][8], yacc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) yacc[c] = 0.f;
     load8<kBf16>(f, t * d + e, fv);
 #pragma unroll
     for (int j = 0; j < kMaxHC; ++j)
@@ -302,7 +324,15 @@ __global__ __launch_bounds__(kGBlock) void post_generic_kernel(const void* __res
             for (int c = 0; c < 8; ++c) o[c] = fmaf(cjk, rv[j][c], o[c]);
         }
         store8<kBf16, kStream>(out, (t * hc + k) * d + e, o);
+        if constexpr (kCollapse) {
+            const float pk = pre_mix[t * hc + k];
+            float r[8];
+            stored8<kBf16>(o, r);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) yacc[c] = fmaf(pk, r[c], yacc[c]);
+        }
     }
+    if constexpr (kCollapse) store8<kBf16>(y, t * d + e, yacc);
 }
 
 // ------------------------------------------------------------- projection
@@ -1273,22 +1303,37 @@ hipError_t launch_pre_generic(const void* x, bool bf16, const float* pre_mix, in
     return hipGetLastError();
 }
 
-hipError_t launch_post_generic(const void* f, const void* res, bool bf16, const float* post, const float* comb,
-                               int64_t n, int hc, int64_t d, void* out, hipStream_t stream, bool stream_out) {
+template <bool kBf16, bool kStream>
+void launch_post_generic_v(dim3 grid, const void* f, const void* res, const float* post, const float* comb, int64_t n,
+                           int hc, int64_t d, void* out, const float* pre_mix, void* y, hipStream_t stream) {
+    if (y)
+        hipLaunchKernelGGL((post_generic_kernel<kBf16, kStream, true>), grid, dim3(kGBlock), 0, stream, f, res, post,
+                           comb, n, hc, d, out, pre_mix, y);
+    else
+        hipLaunchKernelGGL((post_generic_kernel<kBf16, kStream, false>), grid, dim3(kGBlock), 0, stream, f, res, post,
+                           comb, n, hc, d, out, nullptr, nullptr);
+}
+
+// y not null: also the collapse of the new streams with pre_mix into y.
+hipError_t launch_post_collapse_generic(const void* f, const void* res, bool bf16, const float* post,
+                                        const float* comb, int64_t n, int hc, int64_t d, void* out, hipStream_t stream,
+                                        bool stream_out, const float* pre_mix, void* y) {
     const dim3 grid((unsigned)wave_grid(n, d));
     if (bf16 && stream_out)
-        hipLaunchKernelGGL((post_generic_kernel<true, true>), grid, dim3(kGBlock), 0, stream, f, res, post, comb, n,
-                           hc, d, out);
+        launch_post_generic_v<true, true>(grid, f, res, post, comb, n, hc, d, out, pre_mix, y, stream);
     else if (bf16)
-        hipLaunchKernelGGL((post_generic_kernel<true, false>), grid, dim3(kGBlock), 0, stream, f, res, post, comb, n,
-                           hc, d, out);
+        launch_post_generic_v<true, false>(grid, f, res, post, comb, n, hc, d, out, pre_mix, y, stream);
     else if (stream_out)
-        hipLaunchKernelGGL((post_generic_kernel<false, true>), grid, dim3(kGBlock), 0, stream, f, res, post, comb, n,
-                           hc, d, out);
+        launch_post_generic_v<false, true>(grid, f, res, post, comb, n, hc, d, out, pre_mix, y, stream);
     else
-        hipLaunchKernelGGL((post_generic_kernel<false, false>), grid, dim3(kGBlock), 0, stream, f, res, post, comb,
-                           n, hc, d, out);
+        launch_post_generic_v<false, false>(grid, f, res, post, comb, n, hc, d, out, pre_mix, y, stream);
     return hipGetLastError();
+}
+
+hipError_t launch_post_generic(const void* f, const void* res, bool bf16, const float* post, const float* comb,
+                               int64_t n, int hc, int64_t d, void* out, hipStream_t stream, bool stream_out) {
+    return launch_post_collapse_generic(f, res, bf16, post, comb, n, hc, d, out, stream, stream_out, nullptr,
+                                        nullptr);
 }
 
 hipError_t launch_mixes_generic(const void* x, bool bf16, int64_t n, int hc, int64_t d, const float* hc_fn,
@@ -1306,13 +1351,17 @@ hipError_t launch_mixes_generic(const void* x, bool bf16, int64_t n, int hc, int
 constexpr int64_t kLastLevelCacheBytes = int64_t(256) << 20;
 
 hipError_t launch_fused_generic(const GenericRequest& r, hipStream_t stream) {
-    const bool fused_pre = r.bf16 && r.y;
+    // With an expand, the expand kernel also collapses the new streams (it holds
+    // every stream of its channels); otherwise bf16 streams are collapsed inside
+    // the projection and fp32 streams by a collapse kernel after it.
+    const bool fused_pre = r.bf16 && r.y && !r.f_prev;
     const SplitArgs sp{r.scale, r.base, r.iters, r.eps, r.pre, r.post, r.comb};
     const void* src = r.res;
     if (r.f_prev) {
         const int64_t out_bytes = r.n * r.hc * r.d * (r.bf16 ? 2 : 4);
-        if (hipError_t e = launch_post_generic(r.f_prev, r.res, r.bf16, r.post_prev, r.comb_prev, r.n, r.hc, r.d,
-                                               r.streams_out, stream, out_bytes > kLastLevelCacheBytes);
+        if (hipError_t e = launch_post_collapse_generic(r.f_prev, r.res, r.bf16, r.post_prev, r.comb_prev, r.n, r.hc,
+                                                        r.d, r.streams_out, stream, out_bytes > kLastLevelCacheBytes,
+                                                        r.y ? r.pre_mix : nullptr, r.y);
             e != hipSuccess)
             return e;
         src = r.streams_out;
@@ -1322,7 +1371,7 @@ hipError_t launch_fused_generic(const GenericRequest& r, hipStream_t stream) {
                                          fused_pre ? r.pre_mix : nullptr, fused_pre ? r.y : nullptr, stream, &sp);
         e != hipSuccess)
         return e;
-    if (r.y && !fused_pre) return launch_pre_generic(src, r.bf16, r.pre_mix, r.n, r.hc, r.d, r.y, stream);
+    if (r.y && !fused_pre && !r.f_prev) return launch_pre_generic(src, r.bf16, r.pre_mix, r.n, r.hc, r.d, r.y, stream);
     return hipSuccess;
 }
 
