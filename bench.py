@@ -190,13 +190,13 @@ def stream_mix_ceilings(dev, rows: int = 4096, row_bytes: int = 5120 * 2, reps: 
 
 def mfma_ceiling(dev, iters: int = 2000, reps: int = 5):
     """Sustained rate of v_mfma_f32_16x16x32_bf16 (bench_ceilings.hip: eight
-    independent accumulators per wave, no memory traffic), in TFLOP/s, at 1024
-    and 2048 workgroups of 4 waves; median of `reps`. Returns (best, all figures)."""
+    independent accumulators per wave, no memory traffic), in TFLOP/s, at 1024,
+    2048 and 4096 workgroups of 4 waves; median of `reps`. Returns (best, all figures)."""
     import torch
     L = _ceilings_lib()
     stream = torch.cuda.current_stream(dev)
     figures = {}
-    for wgs in (1024, 2048):
+    for wgs in (1024, 2048, 4096):
         out = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
 
         def run():
