@@ -166,8 +166,12 @@ __global__ __launch_bounds__(kGBlock) void split_generic_kernel(const float* __r
 // each. Two streams: a row is a lane pair (quad swap by 1) and a column lanes k
 // and k + 2 (quad swap by 2). Eight streams: a row takes two quad swaps and a
 // half-row mirror (DPP); a column a rotation by 8 within each 16-lane row (DPP),
-// then xor shuffles by 16 and 32. Every partner pair adds the same two numbers,
-// so all lanes of a row (column) end with the same sum. Lanes past kH * kH
+// then sums across 16-lane rows and 32-lane halves with gfx950's lane swaps
+// (v_permlane16_swap / v_permlane32_swap: with both operands the same value, the
+// two results hold each lane's own value and its partner's, in an order that
+// depends on the row, so their sum is the lane's value plus its partner's).
+// Every partner pair adds the same two numbers, so all lanes of a row (column)
+// end with the same sum. Lanes past kH * kH
 // compute on row 0 and store nothing. Otherwise the same steps as
 // split_generic_kernel.
 template <int kCtrl>
@@ -194,12 +198,24 @@ __device__ __forceinline__ float row_max_b(float v) {
     }
     return v;
 }
+// v plus the value of lane l ^ 16 (kSpan 16) or l ^ 32 (kSpan 32), every lane active
+template <int kSpan>
+__device__ __forceinline__ float add_partner(float v) {
+    const uint32_t u = __float_as_uint(v);
+    if constexpr (kSpan == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+}
 template <int kH>
 __device__ __forceinline__ float col_sum_b(float v) {
     if constexpr (kH == 2) return v + dpp_g<kDppQuad2>(v);
     v += dpp_g<kDppRor8>(v);
-    v += __shfl_xor(v, 16);
-    return v + __shfl_xor(v, 32);
+    v = add_partner<16>(v);
+    return add_partner<32>(v);
 }
 
 template <int kH, class Mix>
