@@ -907,7 +907,10 @@ struct SweepLds {
     float ss[kSwWaves][4][16];             // Gram diagonals per wave and tile
 };
 
-template <bool kPost, bool kPre>
+// kOne: every slice is a single step (decode: 64 tokens, 80 slices of 64
+// channels); no loads are issued ahead, since they would all be masked and at
+// this size every wave instruction is on the critical path.
+template <bool kPost, bool kPre, bool kOne>
 __global__ __launch_bounds__(kSwBlock) void bf16_sweep_kernel(PassArgs a) {
     __shared__ SweepLds lds;
 
@@ -994,9 +997,12 @@ __global__ __launch_bounds__(kSwBlock) void bf16_sweep_kernel(PassArgs a) {
 #pragma unroll
     for (int T = 0; T < 4; ++T) acc[T][0] = acc[T][1] = gram[T] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto step = [&](int s, StepRegs<kPost>& cur, StepRegs<kPost>& ahead, float4 (&Wcur)[4], float4 (&Wnext)[4]) {
-        load_b(Wnext, s + 1);
-        load_step(ahead, s + 2);
+    auto step = [&](int s, StepRegs<kPost>& cur, StepRegs<kPost>& ahead, float4 (&Wcur)[4], float4 (&Wnext)[4],
+                    bool prefetch = true) {
+        if (prefetch) {
+            load_b(Wnext, s + 1);
+            load_step(ahead, s + 2);
+        }
         const int64_t cs = c_begin + (int64_t)s * kStep;
         const bool ok = cs + c8 * 8 < c_end;
         const uint32_t vx = ok ? lane_x : kOffMasked, vf = ok ? lane_f : kOffMasked;
@@ -1068,24 +1074,28 @@ __global__ __launch_bounds__(kSwBlock) void bf16_sweep_kernel(PassArgs a) {
     float4 B0[4], B1[4];
     load_b(B0, 0);
     load_step(R0, 0);
-    load_step(R1, 1);
-    // Whole groups of six steps in a loop without exits, the remaining steps
-    // after it: the loads pending at the loop head are then the same on every
-    // path into it, and the compiler need not drain them there.
-    int s = 0;
-    for (; s + 6 <= nst; s += 6) {
-        step(s, R0, R2, B0, B1);
-        step(s + 1, R1, R0, B1, B0);
-        step(s + 2, R2, R1, B0, B1);
-        step(s + 3, R0, R2, B1, B0);
-        step(s + 4, R1, R0, B0, B1);
-        step(s + 5, R2, R1, B1, B0);
+    if constexpr (kOne) {
+        step(0, R0, R2, B0, B1, false);
+    } else {
+        load_step(R1, 1);
+        // Whole groups of six steps in a loop without exits, the remaining steps
+        // after it: the loads pending at the loop head are then the same on every
+        // path into it, and the compiler need not drain them there.
+        int s = 0;
+        for (; s + 6 <= nst; s += 6) {
+            step(s, R0, R2, B0, B1);
+            step(s + 1, R1, R0, B1, B0);
+            step(s + 2, R2, R1, B0, B1);
+            step(s + 3, R0, R2, B1, B0);
+            step(s + 4, R1, R0, B0, B1);
+            step(s + 5, R2, R1, B1, B0);
+        }
+        if (s < nst) step(s, R0, R2, B0, B1);
+        if (s + 1 < nst) step(s + 1, R1, R0, B1, B0);
+        if (s + 2 < nst) step(s + 2, R2, R1, B0, B1);
+        if (s + 3 < nst) step(s + 3, R0, R2, B1, B0);
+        if (s + 4 < nst) step(s + 4, R1, R0, B0, B1);
     }
-    if (s < nst) step(s, R0, R2, B0, B1);
-    if (s + 1 < nst) step(s + 1, R1, R0, B1, B0);
-    if (s + 2 < nst) step(s + 2, R2, R1, B0, B1);
-    if (s + 3 < nst) step(s + 3, R0, R2, B1, B0);
-    if (s + 4 < nst) step(s + 4, R1, R0, B0, B1);
 
     __syncthreads();   // every wave is done with the A buffers
 #pragma unroll
@@ -1741,9 +1751,12 @@ void launch_sweep_t(const PassArgs& a, const PassPlan& p, hipStream_t stream) {
     if (p.wide)
         hipLaunchKernelGGL((bf16_sweep2_kernel<kPost, kPre>), dim3((unsigned)(p.tiles * p.nsplit)), dim3(kSwBlock),
                            0, stream, a);
+    else if (p.chunks_per_split <= kStepKb)   // every slice one step
+        hipLaunchKernelGGL((bf16_sweep_kernel<kPost, kPre, true>), dim3((unsigned)(p.tiles * p.nsplit)),
+                           dim3(kSwBlock), 0, stream, a);
     else
-        hipLaunchKernelGGL((bf16_sweep_kernel<kPost, kPre>), dim3((unsigned)(p.tiles * p.nsplit)), dim3(kSwBlock),
-                           0, stream, a);
+        hipLaunchKernelGGL((bf16_sweep_kernel<kPost, kPre, false>), dim3((unsigned)(p.tiles * p.nsplit)),
+                           dim3(kSwBlock), 0, stream, a);
 }
 
 template <bool kPost, bool kPre>
