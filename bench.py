@@ -347,11 +347,11 @@ def decode_latency(dev, reps: int = 300):
             "algorithmic_bytes": block_bytes, "achieved_gb_s_graph": block_bytes / graph_wall / 1e9}
 
 
-def generic_hc_blocks(dev, steps: int = 20, warmup: int = 20):
+def generic_hc_blocks(dev, steps: int = 20, warmup: int = 100):
     """The prefill block (4096 tokens x hc streams x 5120 bf16) at stream counts
     other than four, which run one kernel per step; timed with HIP events around
-    `steps` blocks after `warmup` blocks (with 2 warm-up blocks the GPU's clocks were
-    still rising: 534-541 us at hc = 8 against 494-495 us after 100)."""
+    `steps` blocks after `warmup` blocks, the steady state (after 20 warm-up blocks
+    the hc = 8 block still measured 470-473 us, after 100 462-466 us)."""
     import torch
     import hc_inputs
     import hyper_connection_residual_mixes_amd as hc
