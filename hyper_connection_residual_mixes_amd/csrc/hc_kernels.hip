@@ -781,12 +781,29 @@ __global__ __launch_bounds__(kFinBlock) void finalize_kernel(FinalizeArgs f) {
 // A wave per token, for many slices: lane l reads float4 l % 8 (entries
 // 4 (l % 8) .. + 3) of slices l / 8, l / 8 + 8, ...; every load is issued before
 // the first wait, and slices past nsplit read as zero (masked offsets). The 8
-// slice groups are then summed by xor shuffles in a fixed order, and each 16-lane
-// group gathers entries e and 16 + e for the coefficient step (all four groups
-// hold the same token; the first stores).
+// slice groups are then summed by an xor tree in a fixed order (lane l + lane
+// l ^ 8 by a row rotation, then l ^ 16 and l ^ 32 by gfx950's lane swaps), and
+// each 16-lane group takes entries e and 16 + e from the 32 sums, passed through
+// the wave's own LDS row, for the coefficient step (all four groups hold the same
+// token; the first stores).
 constexpr int kFinWaveRounds = 16;   // slices per lane: nsplit <= 128
 
+// v + the value of lane l ^ kSpan (kSpan = 16 or 32): gfx950's lane swaps with
+// both operands v return v and its partner, one in each result.
+template <int kSpan>
+__device__ __forceinline__ float add_partner(float v) {
+    const uint32_t u = __float_as_uint(v);
+    if constexpr (kSpan == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+}
+
 __global__ __launch_bounds__(kFinBlock) void finalize_wave_kernel(FinalizeArgs f) {
+    __shared__ float4 sums[kFinBlock / 64][8];
     const int lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * (kFinBlock / 64) + uniform(threadIdx.x >> 6);
     const bool ok = t < f.n;
@@ -812,19 +829,19 @@ __global__ __launch_bounds__(kFinBlock) void finalize_wave_kernel(FinalizeArgs f
     for (int k = 1; k < kFinWaveRounds; ++k) {
         acc.x += v[k].x; acc.y += v[k].y; acc.z += v[k].z; acc.w += v[k].w;
     }
-#pragma unroll
-    for (int m = 8; m <= 32; m <<= 1) {
-        acc.x += __shfl_xor(acc.x, m); acc.y += __shfl_xor(acc.y, m);
-        acc.z += __shfl_xor(acc.z, m); acc.w += __shfl_xor(acc.w, m);
-    }
-    // entry e sits in component e % 4 of lane e / 4; entry 16 + e in lane 4 + e / 4
-    const int e = lane & 15, c = e & 3;
-    const float4 p0 = make_float4(__shfl(acc.x, e >> 2), __shfl(acc.y, e >> 2), __shfl(acc.z, e >> 2),
-                                  __shfl(acc.w, e >> 2));
-    const float4 p1 = make_float4(__shfl(acc.x, 4 + (e >> 2)), __shfl(acc.y, 4 + (e >> 2)),
-                                  __shfl(acc.z, 4 + (e >> 2)), __shfl(acc.w, 4 + (e >> 2)));
-    const float a0 = c == 0 ? p0.x : c == 1 ? p0.y : c == 2 ? p0.z : p0.w;
-    const float a1 = c == 0 ? p1.x : c == 1 ? p1.y : c == 2 ? p1.z : p1.w;
+    acc.x += dpp<kRowRor8>(acc.x); acc.y += dpp<kRowRor8>(acc.y);
+    acc.z += dpp<kRowRor8>(acc.z); acc.w += dpp<kRowRor8>(acc.w);
+    acc.x = add_partner<16>(acc.x); acc.y = add_partner<16>(acc.y);
+    acc.z = add_partner<16>(acc.z); acc.w = add_partner<16>(acc.w);
+    acc.x = add_partner<32>(acc.x); acc.y = add_partner<32>(acc.y);
+    acc.z = add_partner<32>(acc.z); acc.w = add_partner<32>(acc.w);
+    // lanes 0..7 hold entries 4 l .. 4 l + 3 of the sum; the LDS operations of one
+    // wave complete in order, so its reads below see its writes
+    float4* row = sums[threadIdx.x >> 6];
+    if (lane < 8) row[lane] = acc;
+    const int e = lane & 15;
+    const float a0 = reinterpret_cast<const float*>(row)[e];
+    const float a1 = reinterpret_cast<const float*>(row)[16 + e];
     finalize_coeffs(f, cp, t, e, a0, a1, ok && lane < 16);
 }
 
@@ -906,6 +923,28 @@ struct SweepLds {
     uint4 a[2][kSwASlots];                 // 64 KB; reused for the cross-wave reduction
     float ss[kSwWaves][4][16];             // Gram diagonals per wave and tile
 };
+
+// The cross-wave sum of the MFMA accumulators, after every wave has written its
+// own to red[wave][T][nt][lane] (kT 16-token row tiles, 2 mix tiles): thread
+// (T, nt, l) adds the 8 waves' float4s in wave order and stores its 4 tokens'
+// dots (accumulator entry ii of lane l is token 16 T + 4 (l / 16) + ii, mix
+// 16 nt + l % 16).
+template <int kT>
+__device__ __forceinline__ void red_store(const floatx4_t* red, float* __restrict__ part, int64_t tok0, int64_t n) {
+#pragma unroll
+    for (int e = threadIdx.x; e < kT * 2 * 64; e += kSwBlock) {
+        const int l = e & 63, nt = (e >> 6) & 1, T = e >> 7;
+        floatx4_t sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < kSwWaves; ++w) sum += red[w * kT * 2 * 64 + e];
+        const int mix = nt * 16 + (l & 15);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int64_t t = tok0 + T * 16 + 4 * (l >> 4) + ii;
+            if (mix < kMix && t < n) part[t * kPart + mix] = sum[ii];
+        }
+    }
+}
 
 // kOne: every slice is a single step (decode: 64 tokens, 80 slices of 64
 // channels); no loads are issued ahead, since they would all be masked and at
@@ -1102,13 +1141,11 @@ __global__ __launch_bounds__(kSwBlock) void bf16_sweep_kernel(PassArgs a) {
     for (int T = 0; T < 4; ++T)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) acc[T][1][ii] += dpp<kRowRor8>(acc[T][1][ii]);
-    float* red = reinterpret_cast<float*>(&lds.a[0][0]);   // [wave][T][nt][ii][lane], 64 KB
+    floatx4_t* red = reinterpret_cast<floatx4_t*>(&lds.a[0][0]);   // [wave][T][nt][lane], 64 KB
 #pragma unroll
     for (int T = 0; T < 4; ++T)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) red[(((wave * 4 + T) * 2 + nt) * 4 + ii) * 64 + lane] = acc[T][nt][ii];
+        for (int nt = 0; nt < 2; ++nt) red[((wave * 4 + T) * 2 + nt) * 64 + lane] = acc[T][nt];
 #pragma unroll
     for (int T = 0; T < 4; ++T)
 #pragma unroll
@@ -1116,17 +1153,7 @@ __global__ __launch_bounds__(kSwBlock) void bf16_sweep_kernel(PassArgs a) {
             if (col == 4 * g + ii) lds.ss[wave][T][col] = gram[T][ii];
     __syncthreads();
     float* part = a.part + (int64_t)split * n * kPart;
-    for (int e = threadIdx.x; e < 4 * 2 * 4 * 64; e += kSwBlock) {
-        const int l = e & 63, ii = (e >> 6) & 3, nt = (e >> 8) & 1, T = e >> 9;
-        const int mix = nt * 16 + (l & 15);
-        const int64_t t = tok0 + T * 16 + 4 * (l >> 4) + ii;
-        if (mix < kMix && t < n) {
-            float s = 0.f;
-#pragma unroll
-            for (int w = 0; w < kSwWaves; ++w) s += red[w * 2048 + e];
-            part[t * kPart + mix] = s;
-        }
-    }
+    red_store<4>(red, part, tok0, n);
     if (threadIdx.x < kSwTok) {   // token T*16 + row of the group
         const int T = threadIdx.x >> 4, row = threadIdx.x & 15;
         const int64_t t = tok0 + threadIdx.x;
@@ -1357,13 +1384,11 @@ __global__ __launch_bounds__(kSwBlock) void bf16_sweep2_kernel(PassArgs a) {
     for (int T = 0; T < 8; ++T)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) acc[T][1][ii] += dpp<kRowRor8>(acc[T][1][ii]);
-    float* red = reinterpret_cast<float*>(&lds.a[0][0]);   // [wave][T][nt][ii][lane], 128 KB
+    floatx4_t* red = reinterpret_cast<floatx4_t*>(&lds.a[0][0]);   // [wave][T][nt][lane], 128 KB
 #pragma unroll
     for (int T = 0; T < 8; ++T)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) red[(((wave * 8 + T) * 2 + nt) * 4 + ii) * 64 + lane] = acc[T][nt][ii];
+        for (int nt = 0; nt < 2; ++nt) red[((wave * 8 + T) * 2 + nt) * 64 + lane] = acc[T][nt];
     float* part = a.part + (int64_t)split * n * kPart;
     // sum of squares: the 8 lanes of a token row (xor 1, 2, 4), in a fixed order
 #pragma unroll
@@ -1376,17 +1401,7 @@ __global__ __launch_bounds__(kSwBlock) void bf16_sweep2_kernel(PassArgs a) {
         if (c8 == 0 && t < n) part[t * kPart + kMix] = v;
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < 8 * 2 * 4 * 64; e += kSwBlock) {
-        const int l = e & 63, ii = (e >> 6) & 3, nt = (e >> 8) & 1, T = e >> 9;
-        const int mix = nt * 16 + (l & 15);
-        const int64_t t = tok0 + T * 16 + 4 * (l >> 4) + ii;
-        if (mix < kMix && t < n) {
-            float sum = 0.f;
-#pragma unroll
-            for (int w = 0; w < kSwWaves; ++w) sum += red[w * 4096 + e];
-            part[t * kPart + mix] = sum;
-        }
-    }
+    red_store<8>(red, part, tok0, n);
 }
 
 // ------------------------------------------- sublayer RMSNorm + MXFP8 cast
