@@ -970,26 +970,32 @@ __global__ __launch_bounds__(kSwBlock) void bf16_sweep_kernel(PassArgs a) {
     const int64_t c_end = min(d, (int64_t)kb_end * kChunk);
     const int nst = (int)((c_end - c_begin + kStep - 1) / kStep);   // >= 1: slices are never empty
 
+    // The token's coefficients, as raw buffer loads (a token past n reads zeros):
+    // no branch, so nothing waits for them before the rowwise work uses them. A
+    // guarded load inside a branch made the compiler wait for it at the branch's
+    // end, a memory round trip before the first stream load was issued.
     float pk[kHC], cm[kHC * kHC], pim[kHC];
 #pragma unroll
     for (int i = 0; i < kHC; ++i) pk[i] = pim[i] = 0.f;
 #pragma unroll
     for (int i = 0; i < kHC * kHC; ++i) cm[i] = 0.f;
-    if (tok_ok) {
-        const int64_t t = tok0 + tl;
-        if constexpr (kPost) {
-            const float4 pv = reinterpret_cast<const float4*>(a.post_prev)[t];
-            pk[0] = pv.x; pk[1] = pv.y; pk[2] = pv.z; pk[3] = pv.w;
+    const uint32_t lane_c = tok_ok ? (uint32_t)(tl * 16) : kOffMasked;   // 16 B per token and row of 4
+    if constexpr (kPost) {
+        const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.post_prev + tok0 * kHC, (n - tok0) * 16);
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.comb_prev + tok0 * kHC * kHC, (n - tok0) * 64);
+        const uint32_t lane_cc = tok_ok ? (uint32_t)(tl * 64) : kOffMasked;
+        const float4 pv = buf_load16f(rp, lane_c, 0);
+        pk[0] = pv.x; pk[1] = pv.y; pk[2] = pv.z; pk[3] = pv.w;
 #pragma unroll
-            for (int j = 0; j < kHC; ++j) {
-                const float4 cv = reinterpret_cast<const float4*>(a.comb_prev)[t * kHC + j];
-                cm[4 * j] = cv.x; cm[4 * j + 1] = cv.y; cm[4 * j + 2] = cv.z; cm[4 * j + 3] = cv.w;
-            }
+        for (int j = 0; j < kHC; ++j) {
+            const float4 cv = buf_load16f(rc, lane_cc, (uint32_t)(j * 16));
+            cm[4 * j] = cv.x; cm[4 * j + 1] = cv.y; cm[4 * j + 2] = cv.z; cm[4 * j + 3] = cv.w;
         }
-        if constexpr (kPre) {
-            const float4 pv = reinterpret_cast<const float4*>(a.pre_mix)[t];
-            pim[0] = pv.x; pim[1] = pv.y; pim[2] = pv.z; pim[3] = pv.w;
-        }
+    }
+    if constexpr (kPre) {
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.pre_mix + tok0 * kHC, (n - tok0) * 16);
+        const float4 pv = buf_load16f(rq, lane_c, 0);
+        pim[0] = pv.x; pim[1] = pv.y; pim[2] = pv.z; pim[3] = pv.w;
     }
 
     const int64_t row_x = kHC * d * 2, row_f = d * 2;
