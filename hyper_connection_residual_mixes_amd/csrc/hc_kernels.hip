@@ -384,6 +384,16 @@ struct PassArgs {
     int nsplit;
 };
 
+// A kernel's arguments are read by scalar loads that the compiler issues at
+// their first use, so a use behind another load's wait costs one more memory
+// round trip. Naming every field in an empty asm at entry has all of them
+// issued together, with one wait.
+__device__ __forceinline__ void pin_args(const PassArgs& a) {
+    asm volatile("" ::"s"(a.res), "s"(a.f), "s"(a.post_prev), "s"(a.comb_prev), "s"(a.pre_mix), "s"(a.hc_fn),
+                 "s"(a.streams_out), "s"(a.y), "s"(a.part), "s"(a.n), "s"(a.d), "s"(a.nchunks),
+                 "s"(a.chunks_per_split), "s"(a.nsplit));
+}
+
 constexpr int kPassBlock = kWaves * 64;
 constexpr int kF32Row = kHC * kChunk + 4;      // floats per mix row of the fp32 stage (padded)
 constexpr int kF32Stage = 32 * kF32Row;        // floats per LDS buffer: 32 mix rows (24..31 zero)
@@ -687,20 +697,31 @@ struct FinalizeArgs {
     float* comb;
 };
 
+__device__ __forceinline__ void pin_args(const FinalizeArgs& f) {
+    asm volatile("" ::"s"(f.part), "s"(f.nsplit), "s"(f.n), "s"(f.D), "s"(f.norm_eps), "s"(f.scale), "s"(f.base),
+                 "s"(f.iters), "s"(f.eps), "s"((int)f.split), "s"(f.mixes), "s"(f.pre), "s"(f.post), "s"(f.comb));
+}
+
 // The split parameters lane e of a 16-lane group needs, fetched before the
 // partial rows so that both are in flight together.
 struct CoefParams {
     float s0, s1, s2, b_e, b_8e;   // hc_scale[0..2], hc_base[e], hc_base[8 + e]
 };
+// Raw buffer loads with empty ranges when there is no split (they return zeros):
+// no branch, so they are issued with the partial rows' loads instead of after a
+// wait for the parameter pointers.
+__device__ __forceinline__ float buf_load4f(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0));
+}
 __device__ __forceinline__ CoefParams load_coef_params(const FinalizeArgs& f, int e) {
-    CoefParams c{};
-    if (f.split) {   // uniform
-        c.s0 = f.scale[0];
-        c.s1 = f.scale[1];
-        c.s2 = f.scale[2];
-        c.b_e = f.base[e];
-        c.b_8e = f.base[8 + e];
-    }
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(f.split ? f.scale : nullptr, f.split ? 3 * 4 : 0);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(f.split ? f.base : nullptr, f.split ? kMix * 4 : 0);
+    CoefParams c;
+    c.s0 = buf_load4f(rs, 0);
+    c.s1 = buf_load4f(rs, 4);
+    c.s2 = buf_load4f(rs, 8);
+    c.b_e = buf_load4f(rb, (uint32_t)e * 4);
+    c.b_8e = buf_load4f(rb, (uint32_t)(8 + e) * 4);
     return c;
 }
 
@@ -775,6 +796,7 @@ __device__ __forceinline__ void finalize16(const FinalizeArgs& f, int64_t t, int
 constexpr int kFinBlock = 256;
 
 __global__ __launch_bounds__(kFinBlock) void finalize_kernel(FinalizeArgs f) {
+    pin_args(f);
     finalize16(f, ((int64_t)blockIdx.x * kFinBlock + threadIdx.x) >> 4, threadIdx.x & 15);
 }
 
@@ -804,6 +826,7 @@ __device__ __forceinline__ float add_partner(float v) {
 
 __global__ __launch_bounds__(kFinBlock) void finalize_wave_kernel(FinalizeArgs f) {
     __shared__ float4 sums[kFinBlock / 64][8];
+    pin_args(f);
     const int lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * (kFinBlock / 64) + uniform(threadIdx.x >> 6);
     const bool ok = t < f.n;
@@ -952,6 +975,7 @@ __device__ __forceinline__ void red_store(const floatx4_t* red, float* __restric
 template <bool kPost, bool kPre, bool kOne>
 __global__ __launch_bounds__(kSwBlock) void bf16_sweep_kernel(PassArgs a) {
     __shared__ SweepLds lds;
+    pin_args(a);
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1200,6 +1224,7 @@ struct StepRegs2 {
 template <bool kPost, bool kPre>
 __global__ __launch_bounds__(kSwBlock) void bf16_sweep2_kernel(PassArgs a) {
     __shared__ Sweep2Lds lds;
+    pin_args(a);
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
