@@ -1242,17 +1242,6 @@ __global__ __launch_bounds__(kSwBlock) void bf16_sweep2_kernel(PassArgs a) {
     const int64_t c_end = min(d, (int64_t)kb_end * kChunk);
     const int nst = (int)((c_end - c_begin + kStep - 1) / kStep);
 
-    for (int i = threadIdx.x; i < kS2Tok * kS2Coef; i += kSwBlock) {
-        const int t = i / kS2Coef, q = i - t * kS2Coef;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (tok0 + t < n) {
-            if (kPost && q == 0) v = reinterpret_cast<const float4*>(a.post_prev)[tok0 + t];
-            if (kPost && q >= 1 && q <= 4) v = reinterpret_cast<const float4*>(a.comb_prev)[(tok0 + t) * kHC + q - 1];
-            if (kPre && q == 5) v = reinterpret_cast<const float4*>(a.pre_mix)[tok0 + t];
-        }
-        lds.coef[t][q] = v;
-    }
-
     const int64_t row_x = kHC * d * 2, row_f = d * 2;
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(static_cast<const char*>(a.res) + tok0 * row_x, (n - tok0) * row_x);
     const __amdgpu_buffer_rsrc_t rf = make_rsrc(kPost ? static_cast<const char*>(a.f) + tok0 * row_f : nullptr,
@@ -1397,11 +1386,48 @@ __global__ __launch_bounds__(kSwBlock) void bf16_sweep2_kernel(PassArgs a) {
         }
     };
 
+    // The per-token coefficients go to LDS, loaded with the first step's loads
+    // and written after those are issued (a load behind a branch, written at
+    // once, would make every wave wait a memory round trip before its first
+    // stream load). Item i of the list [post (128) | comb rows (4 x 128) | pre_mix
+    // (128)], as far as the instance uses them, is thread i % 512's load r = i /
+    // 512; each wave's 64 items come from one array, so the source is uniform.
+    // Tokens past n read as zeros (the buffer ranges end at n).
+    constexpr int kNPost = kPost ? kS2Tok : 0, kNComb = kPost ? kS2Tok * kHC : 0, kNPre = kPre ? kS2Tok : 0;
+    constexpr int kNCoef = kNPost + kNComb + kNPre;
+    constexpr int kCoefLoads = (kNCoef + kSwBlock - 1) / kSwBlock;
+    const __amdgpu_buffer_rsrc_t rcp = make_rsrc(kPost ? a.post_prev + tok0 * kHC : nullptr, kPost ? (n - tok0) * 16 : 0);
+    const __amdgpu_buffer_rsrc_t rcc =
+        make_rsrc(kPost ? a.comb_prev + tok0 * kHC * kHC : nullptr, kPost ? (n - tok0) * 64 : 0);
+    const __amdgpu_buffer_rsrc_t rcq = make_rsrc(kPre ? a.pre_mix + tok0 * kHC : nullptr, kPre ? (n - tok0) * 16 : 0);
+    float4 coef_v[kCoefLoads > 0 ? kCoefLoads : 1];
+    auto coef_item = [&](int r, int& first, int& j, int& seg) {   // seg 0 post, 1 comb, 2 pre_mix
+        first = uniform((uint32_t)(r * kSwBlock + wave * 64));
+        const int i = r * kSwBlock + (int)threadIdx.x;
+        seg = first < kNPost ? 0 : first < kNPost + kNComb ? 1 : 2;
+        j = i - (seg == 0 ? 0 : seg == 1 ? kNPost : kNPost + kNComb);
+    };
+#pragma unroll
+    for (int r = 0; r < kCoefLoads; ++r) {
+        int first, j, seg;
+        coef_item(r, first, j, seg);
+        if (first < kNCoef) coef_v[r] = buf_load16f(seg == 0 ? rcp : seg == 1 ? rcc : rcq, (uint32_t)j * 16, 0);
+    }
     StepRegs2<kPost> R0, R1;
     float4 B0[4], B1[4];
     load_b(B0, 0);
     load_step(R0, 0);
     if constexpr (kPost) load_step(R1, 1);
+#pragma unroll
+    for (int r = 0; r < kCoefLoads; ++r) {
+        int first, j, seg;
+        coef_item(r, first, j, seg);
+        if (first < kNCoef) {
+            if (seg == 0) lds.coef[j][0] = coef_v[r];
+            else if (seg == 1) lds.coef[j >> 2][1 + (j & 3)] = coef_v[r];
+            else lds.coef[j][5] = coef_v[r];
+        }
+    }
     __syncthreads();   // the coefficients are in LDS
     int s = 0;
     for (; s + 2 <= nst; s += 2) {
