@@ -1176,11 +1176,15 @@ __global__ __launch_bounds__(kSwBlock) void bf16_sweep_kernel(PassArgs a) {
     for (int T = 0; T < 4; ++T)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) red[((wave * 4 + T) * 2 + nt) * 64 + lane] = acc[T][nt];
+    // Gram diagonal: lane (g, col) holds entry (4 g + ii, col) of each row tile's
+    // A A^T, so at most one diagonal entry per tile, ii = col - 4 g; one
+    // predicated store per tile (a branch per candidate entry cost more)
+    const int dii = col - 4 * g;
 #pragma unroll
-    for (int T = 0; T < 4; ++T)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-            if (col == 4 * g + ii) lds.ss[wave][T][col] = gram[T][ii];
+    for (int T = 0; T < 4; ++T) {
+        const float v = dii == 0 ? gram[T][0] : dii == 1 ? gram[T][1] : dii == 2 ? gram[T][2] : gram[T][3];
+        if ((unsigned)dii < 4u) lds.ss[wave][T][col] = v;
+    }
     __syncthreads();
     float* part = a.part + (int64_t)split * n * kPart;
     red_store<4>(red, part, tok0, n);
