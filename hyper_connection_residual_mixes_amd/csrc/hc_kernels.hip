@@ -1127,15 +1127,21 @@ __global__ __launch_bounds__(kSwBlock) void bf16_sweep_kernel(PassArgs a) {
         Bcur[3] = make_uint4(lo_half ? hi1.x : mid1.x, lo_half ? hi1.y : mid1.y, lo_half ? hi1.z : mid1.z,
                              lo_half ? hi1.w : mid1.w);
         Bcur[4] = make_uint4(lo_half ? lo1.x : 0u, lo_half ? lo1.y : 0u, lo_half ? lo1.z : 0u, lo_half ? lo1.w : 0u);
+        // the four A reads are issued before the first MFMA (a scheduling barrier
+        // keeps them there): otherwise each read's latency sits between two MFMA
+        // groups
+        bf16x8_t Av[4];
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+            Av[T] = __builtin_bit_cast(bf16x8_t, A[a_slot(T * 16 + (lane & 15), mj, mkk * 4 + (lane >> 4))]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int T = 0; T < 4; ++T) {
-            const bf16x8_t Av =
-                __builtin_bit_cast(bf16x8_t, A[a_slot(T * 16 + (lane & 15), mj, mkk * 4 + (lane >> 4))]);
 #pragma unroll
             for (int q = 0; q < kFragsPerKb; ++q)
                 acc[T][q < 3 ? 0 : 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    Av, __builtin_bit_cast(bf16x8_t, Bcur[q]), acc[T][q < 3 ? 0 : 1], 0, 0, 0);
-            gram[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, Av, gram[T], 0, 0, 0);
+                    Av[T], __builtin_bit_cast(bf16x8_t, Bcur[q]), acc[T][q < 3 ? 0 : 1], 0, 0, 0);
+            gram[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av[T], Av[T], gram[T], 0, 0, 0);
         }
     };
 
@@ -1379,14 +1385,35 @@ __global__ __launch_bounds__(kSwBlock) void bf16_sweep2_kernel(PassArgs a) {
         Bcur[3] = make_uint4(lo_half ? hi1.x : mid1.x, lo_half ? hi1.y : mid1.y, lo_half ? hi1.z : mid1.z,
                              lo_half ? hi1.w : mid1.w);
         Bcur[4] = make_uint4(lo_half ? lo1.x : 0u, lo_half ? lo1.y : 0u, lo_half ? lo1.z : 0u, lo_half ? lo1.w : 0u);
+        // Without the expand, each A read is issued one row tile ahead of its MFMAs
+        // (a scheduling barrier keeps it there), so its latency overlaps the
+        // previous tile's MFMAs; the expand instance has no registers to spare for it.
+        if constexpr (kPost) {
 #pragma unroll
-        for (int T = 0; T < 8; ++T) {
-            const bf16x8_t Av =
-                __builtin_bit_cast(bf16x8_t, A[a_slot(T * 16 + (lane & 15), mj, mkk * 4 + (lane >> 4))]);
+            for (int T = 0; T < 8; ++T) {
+                const bf16x8_t Av =
+                    __builtin_bit_cast(bf16x8_t, A[a_slot(T * 16 + (lane & 15), mj, mkk * 4 + (lane >> 4))]);
 #pragma unroll
-            for (int q = 0; q < kFragsPerKb; ++q)
-                acc[T][q < 3 ? 0 : 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    Av, __builtin_bit_cast(bf16x8_t, Bcur[q]), acc[T][q < 3 ? 0 : 1], 0, 0, 0);
+                for (int q = 0; q < kFragsPerKb; ++q)
+                    acc[T][q < 3 ? 0 : 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        Av, __builtin_bit_cast(bf16x8_t, Bcur[q]), acc[T][q < 3 ? 0 : 1], 0, 0, 0);
+            }
+        } else {
+            auto read_a = [&](int T) {
+                return __builtin_bit_cast(bf16x8_t, A[a_slot(T * 16 + (lane & 15), mj, mkk * 4 + (lane >> 4))]);
+            };
+            bf16x8_t Acur = read_a(0);
+#pragma unroll
+            for (int T = 0; T < 8; ++T) {
+                bf16x8_t Anext = Acur;
+                if (T + 1 < 8) Anext = read_a(T + 1);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int q = 0; q < kFragsPerKb; ++q)
+                    acc[T][q < 3 ? 0 : 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        Acur, __builtin_bit_cast(bf16x8_t, Bcur[q]), acc[T][q < 3 ? 0 : 1], 0, 0, 0);
+                Acur = Anext;
+            }
         }
     };
 
