@@ -223,14 +223,19 @@ __device__ __forceinline__ void split_butterfly_wave(const Mix& mix, const float
                                                      const float* __restrict__ base, int64_t t, int iters, float eps,
                                                      float* __restrict__ pre, float* __restrict__ post,
                                                      float* __restrict__ comb) {
+    // No contraction: the compiler would fuse a lane's own product into the first
+    // add of a column sum, while its partner's term arrives rounded, so the lanes
+    // of a column would not add the same two numbers; the fused multiply-adds
+    // meant here are written out.
+#pragma clang fp contract(off)
     static_assert(kH == 2 || kH == 8, "butterflies for two or eight streams");
     const int lane = threadIdx.x & 63;
     const bool cl = lane < kH * kH;
     const int ci = 2 * kH + (cl ? lane : lane % kH);
     const float mp = mix(lane < 2 * kH ? lane : 0);   // pre / post logit of lanes 0 .. 2 kH - 1
-    float c = mix(ci) * scale[2] + base[ci];
+    float c = fmaf(mix(ci), scale[2], base[ci]);
     c = __expf(c - row_max_b<kH>(c));
-    c = c * __builtin_amdgcn_rcpf(row_sum_b<kH>(c)) + eps;
+    c = fmaf(c, __builtin_amdgcn_rcpf(row_sum_b<kH>(c)), eps);
     c *= __builtin_amdgcn_rcpf(col_sum_b<kH>(c) + eps);
     for (int it = 1; it < iters; ++it) {
         c *= __builtin_amdgcn_rcpf(row_sum_b<kH>(c) + eps);
@@ -238,9 +243,9 @@ __device__ __forceinline__ void split_butterfly_wave(const Mix& mix, const float
     }
     if (cl) comb[t * kH * kH + lane] = c;
     if (lane < kH)
-        pre[t * kH + lane] = sigmoid_f(mp * scale[0] + base[lane]) + eps;
+        pre[t * kH + lane] = sigmoid_f(fmaf(mp, scale[0], base[lane])) + eps;
     else if (lane < 2 * kH)
-        post[t * kH + lane - kH] = 2.0f * sigmoid_f(mp * scale[1] + base[lane]);
+        post[t * kH + lane - kH] = 2.0f * sigmoid_f(fmaf(mp, scale[1], base[lane]));
 }
 
 template <int kH>
@@ -1090,6 +1095,91 @@ __global__ __launch_bounds__(kGBlock) void finalize_split_kernel(const float* __
         split_butterfly_wave<kH>(mix, scale, base, t, iters, eps, pre, post, comb);
 }
 
+// Two streams: the finalize and the split with 4 lanes per token (16 tokens per
+// wave; a wave per token left 60 of its 64 lanes idle through the Sinkhorn
+// rounds). Lane q < 3 of a token's quad sums float4 q of its partial rows (12
+// floats: dots 0..7, the sum of squares at 8) over the slices in order; slices
+// past nsplit and lane 3 re-read a valid row and add zero instead. Every lane of
+// the quad then takes lanes 0 and 1's sums (mixes 0..3: pre and post logits,
+// 4..7: the 2 x 2 comb) and runs the same steps as split_butterfly_wave<2> in
+// registers, where a row or column sum is one add of the same two numbers (as in
+// the butterfly, both without contraction), so the results are the same bits;
+// lane 0 stores pre, lane 1 post, lane 2 the comb. Lanes past n compute on token
+// n - 1 and store nothing.
+constexpr int kF2Pg = 12;
+__global__ __launch_bounds__(kGBlock) void finalize_split2_kernel(const float* __restrict__ part, int nsplit,
+                                                                  int64_t n, int64_t d, float norm_eps,
+                                                                  float* __restrict__ mixes,
+                                                                  const float* __restrict__ scale,
+                                                                  const float* __restrict__ base, int iters,
+                                                                  float eps, float* __restrict__ pre,
+                                                                  float* __restrict__ post, float* __restrict__ comb) {
+    // No contraction here: in registers the compiler would fuse a product into the
+    // next row or column sum, which the butterfly (whose sums read other lanes)
+    // cannot; the fused multiply-adds the butterfly does get are written out.
+#pragma clang fp contract(off)
+    const int q = threadIdx.x & 3;
+    const int64_t t = ((int64_t)blockIdx.x * kGBlock + threadIdx.x) >> 2;
+    const bool ok = t < n;
+    const int64_t tt = ok ? t : n - 1;
+    const int qc = q < 3 ? q : 2;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s0 = 0; s0 < nsplit; s0 += 16) {
+        float4 v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int sc = s0 + i < nsplit ? s0 + i : nsplit - 1;
+            v[i] = *reinterpret_cast<const float4*>(part + ((int64_t)sc * n + tt) * kF2Pg + 4 * qc);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const bool keep = s0 + i < nsplit && q < 3;
+            acc.x += keep ? v[i].x : 0.f;
+            acc.y += keep ? v[i].y : 0.f;
+            acc.z += keep ? v[i].z : 0.f;
+            acc.w += keep ? v[i].w : 0.f;
+        }
+    }
+    constexpr int kBcast0 = 0x00, kBcast1 = 0x55, kBcast2 = 0xAA;   // quad_perm: every lane reads lane 0 / 1 / 2
+    const float ss = dpp_g<kBcast2>(acc.x);
+    const float rstd = 1.0f / sqrtf(ss / (float)(2 * d) + norm_eps);
+    const float4 lo = make_float4(dpp_g<kBcast0>(acc.x) * rstd, dpp_g<kBcast0>(acc.y) * rstd,
+                                  dpp_g<kBcast0>(acc.z) * rstd, dpp_g<kBcast0>(acc.w) * rstd);
+    const float4 cm = make_float4(dpp_g<kBcast1>(acc.x) * rstd, dpp_g<kBcast1>(acc.y) * rstd,
+                                  dpp_g<kBcast1>(acc.z) * rstd, dpp_g<kBcast1>(acc.w) * rstd);
+    if (mixes && ok && q < 2)
+        reinterpret_cast<float4*>(mixes)[t * 2 + q] = make_float4(q == 0 ? lo.x : cm.x, q == 0 ? lo.y : cm.y,
+                                                                  q == 0 ? lo.z : cm.z, q == 0 ? lo.w : cm.w);
+    // comb logits C[j][k] = mixes[4 + 2 j + k]
+    float c00 = fmaf(cm.x, scale[2], base[4]), c01 = fmaf(cm.y, scale[2], base[5]);
+    float c10 = fmaf(cm.z, scale[2], base[6]), c11 = fmaf(cm.w, scale[2], base[7]);
+    const float m0 = fmaxf(c00, c01), m1 = fmaxf(c10, c11);
+    c00 = __expf(c00 - m0); c01 = __expf(c01 - m0);
+    c10 = __expf(c10 - m1); c11 = __expf(c11 - m1);
+    float r0 = __builtin_amdgcn_rcpf(c00 + c01), r1 = __builtin_amdgcn_rcpf(c10 + c11);
+    c00 = fmaf(c00, r0, eps); c01 = fmaf(c01, r0, eps);
+    c10 = fmaf(c10, r1, eps); c11 = fmaf(c11, r1, eps);
+    float k0 = __builtin_amdgcn_rcpf(c00 + c10 + eps), k1 = __builtin_amdgcn_rcpf(c01 + c11 + eps);
+    c00 *= k0; c10 *= k0; c01 *= k1; c11 *= k1;
+    for (int it = 1; it < iters; ++it) {
+        r0 = __builtin_amdgcn_rcpf(c00 + c01 + eps);
+        r1 = __builtin_amdgcn_rcpf(c10 + c11 + eps);
+        c00 *= r0; c01 *= r0; c10 *= r1; c11 *= r1;
+        k0 = __builtin_amdgcn_rcpf(c00 + c10 + eps);
+        k1 = __builtin_amdgcn_rcpf(c01 + c11 + eps);
+        c00 *= k0; c10 *= k0; c01 *= k1; c11 *= k1;
+    }
+    if (!ok) return;
+    if (q == 0)
+        reinterpret_cast<float2*>(pre)[t] = make_float2(sigmoid_f(fmaf(lo.x, scale[0], base[0])) + eps,
+                                                        sigmoid_f(fmaf(lo.y, scale[0], base[1])) + eps);
+    else if (q == 1)
+        reinterpret_cast<float2*>(post)[t] = make_float2(2.0f * sigmoid_f(fmaf(lo.z, scale[1], base[2])),
+                                                         2.0f * sigmoid_f(fmaf(lo.w, scale[1], base[3])));
+    else if (q == 2)
+        reinterpret_cast<float4*>(comb)[t] = make_float4(c00, c01, c10, c11);
+}
+
 int64_t ceil_div_g(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct GenericPlan {
@@ -1262,8 +1352,9 @@ hipError_t launch_projection(const void* x, bool bf16, int64_t n, int hc, int64_
         hipLaunchKernelGGL(finalize_split_kernel<8>, grid, dim3(kGBlock), 0, stream, part, p.nsplit, p.pg, n, hc, d,
                            norm_eps, mixes, sp->scale, sp->base, sp->iters, sp->eps, sp->pre, sp->post, sp->comb);
     else if (hc == 2)
-        hipLaunchKernelGGL(finalize_split_kernel<2>, grid, dim3(kGBlock), 0, stream, part, p.nsplit, p.pg, n, hc, d,
-                           norm_eps, mixes, sp->scale, sp->base, sp->iters, sp->eps, sp->pre, sp->post, sp->comb);
+        hipLaunchKernelGGL(finalize_split2_kernel, dim3((unsigned)ceil_div_g(n, kGBlock / 4)), dim3(kGBlock), 0,
+                           stream, part, p.nsplit, n, d, norm_eps, mixes, sp->scale, sp->base, sp->iters, sp->eps,
+                           sp->pre, sp->post, sp->comb);
     else
         hipLaunchKernelGGL(finalize_split_kernel<0>, grid, dim3(kGBlock), 0, stream, part, p.nsplit, p.pg, n, hc, d,
                            norm_eps, mixes, sp->scale, sp->base, sp->iters, sp->eps, sp->pre, sp->post, sp->comb);

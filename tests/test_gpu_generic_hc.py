@@ -170,6 +170,26 @@ def test_fused_exact_inputs_and_in_place(hc_):
     check(f"hc={hc_} y after expand", got2["y"], ref2["y"], TOL_BF16)
 
 
+@pytest.mark.parametrize("hc_,n,iters", [(2, 4096, 20), (2, 37, 7), (2, 1, 1), (8, 300, 20), (8, 5, 3)])
+def test_fused_split_same_bits_as_split(hc_, n, iters):
+    """The split fused into the finalize (four lanes per token at two streams, the
+    butterfly at eight) gives the same bits as hc_split_sinkhorn on the mixes the
+    fused step returns: both run the same fp32 steps, with every lane of a comb row
+    or column adding the same numbers (no contraction of a lane's own product)."""
+    dtype, d = torch.bfloat16, 264
+    x, attn, _, _, _, prev = _block_inputs(hc_, dtype, n, d, seed=90 + hc_)
+    pi = oracle.hc_split_sinkhorn(*prev, hc_mult=hc_)[0]
+    _, scale, base = attn
+    got = hc.hc_fused_step(*to_dev((x,)), *to_dev(attn), pre_mix=to_dev(pi), sinkhorn_iters=iters,
+                           want_mixes=True)
+    pre, post, comb = hc.hc_split_sinkhorn(got["mixes"], *to_dev((scale, base)), hc_mult=hc_,
+                                           sinkhorn_iters=iters)
+    sync()
+    assert torch.equal(got["pre"], pre)
+    assert torch.equal(got["post"], post)
+    assert torch.equal(got["comb"], comb)
+
+
 @pytest.mark.parametrize("hc_", [2, 8])
 def test_block_full_size_sampled(hc_):
     """The prefill block at two and eight streams (4096 tokens x 5120 bf16, 1% x50
