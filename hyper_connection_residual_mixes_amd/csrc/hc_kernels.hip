@@ -731,6 +731,11 @@ __device__ __forceinline__ CoefParams load_coef_params(const FinalizeArgs& f, in
 // write.
 __device__ __forceinline__ void finalize_coeffs(const FinalizeArgs& f, const CoefParams& cp, int64_t t, int e,
                                                 float a0, float a1, bool store) {
+    // No contraction: the compiler would fuse a lane's own product into the first
+    // add of a column sum while the partner's term arrives rounded, so the four
+    // lanes of a comb column would not add the same numbers; the fused
+    // multiply-adds meant here are written out.
+#pragma clang fp contract(off)
     const int lane16 = (threadIdx.x & 63) & ~15;
     const float sumsq = __shfl(a1, lane16 + (kMix - 16));
     const float rstd = 1.0f / sqrtf(sumsq / (float)f.D + f.norm_eps);
@@ -745,12 +750,12 @@ __device__ __forceinline__ void finalize_coeffs(const FinalizeArgs& f, const Coe
     const float lo = __shfl(m0, lane16 + ((8 + e) & 15));
     const float hi = __shfl(m1, lane16 + ((e + 8) & 15));
     const float m = e < 8 ? lo : hi;
-    float c = m * cp.s2 + cp.b_8e;
+    float c = fmaf(m, cp.s2, cp.b_8e);
     // row softmax (max subtracted), + eps
     float mx = fmaxf(c, dpp<kQuadSwap1>(c));
     mx = fmaxf(mx, dpp<kQuadSwap2>(mx));
     c = __expf(c - mx);
-    c = c * __builtin_amdgcn_rcpf(row_sum16(c)) + f.eps;
+    c = fmaf(c, __builtin_amdgcn_rcpf(row_sum16(c)), f.eps);
     c *= __builtin_amdgcn_rcpf(col_sum16(c) + f.eps);
     for (int it = 1; it < f.iters; ++it) {
         c *= __builtin_amdgcn_rcpf(row_sum16(c) + f.eps);
@@ -758,8 +763,8 @@ __device__ __forceinline__ void finalize_coeffs(const FinalizeArgs& f, const Coe
     }
     if (store) {
         f.comb[t * 16 + e] = c;
-        if (e < kHC) f.pre[t * kHC + e] = sigmoid(m0 * cp.s0 + cp.b_e) + f.eps;
-        else if (e < 2 * kHC) f.post[t * kHC + e - kHC] = 2.0f * sigmoid(m0 * cp.s1 + cp.b_e);
+        if (e < kHC) f.pre[t * kHC + e] = sigmoid(fmaf(m0, cp.s0, cp.b_e)) + f.eps;
+        else if (e < 2 * kHC) f.post[t * kHC + e - kHC] = 2.0f * sigmoid(fmaf(m0, cp.s1, cp.b_e));
     }
 }
 
