@@ -1107,6 +1107,7 @@ __global__ __launch_bounds__(kGBlock) void finalize_split_kernel(const float* __
 // lane 0 stores pre, lane 1 post, lane 2 the comb. Lanes past n compute on token
 // n - 1 and store nothing.
 constexpr int kF2Pg = 12;
+static_assert((((2 + 2) * 2 + 1 + 3) & ~3) == kF2Pg, "the plan's partial-row pitch at two streams");
 __global__ __launch_bounds__(kGBlock) void finalize_split2_kernel(const float* __restrict__ part, int nsplit,
                                                                   int64_t n, int64_t d, float norm_eps,
                                                                   float* __restrict__ mixes,
